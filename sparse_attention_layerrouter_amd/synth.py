@@ -1,0 +1,135 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention or routing arithmetic.  Host inputs come from
+``numpy.random.default_rng(seed)`` drawn in a fixed order; large device inputs
+come from a seeded ``torch.Generator`` on the GPU.  bf16 values are produced
+from fp32 by round-to-nearest-even and carried on the host as their uint16 bit
+patterns.
+
+Workload shapes follow the task's configurations: Llama-3.1-8B attention
+(32 query heads, 8 KV heads, head_dim 128) and Qwen3-4B attention (same head
+layout, 36 layers, hidden 2560), the model shapes the pages evaluate on
+[thelatestinai paper page, Tables 1, 15, 18].
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even); return the uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    nan = np.isnan(x)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = rounded.astype(np.uint16)
+    out[nan] = 0x7FC0
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to fp32 exactly."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def xavier_uniform(rng: np.random.Generator, fan_out: int, fan_in: int) -> np.ndarray:
+    """Glorot-uniform weights U(-a, a), a = sqrt(6 / (fan_in + fan_out)), shape [fan_out, fan_in]."""
+    a = math.sqrt(6.0 / (fan_in + fan_out))
+    return rng.uniform(-a, a, size=(fan_out, fan_in)).astype(np.float32)
+
+
+def normal(rng: np.random.Generator, shape, scale: float = 1.0) -> np.ndarray:
+    return (rng.standard_normal(size=shape) * scale).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Tiny case: 2 layers, 4 query heads / 2 KV heads, head_dim 64, fp32, T=256.
+# ---------------------------------------------------------------------------
+
+TINY = dict(n_layers=2, hq=4, hkv=2, d=64, seq=256, hidden=256, router_hidden=16,
+            sink=16, window=64, block=16, pool=64)
+
+
+def tiny_case(seed: int = 0) -> dict:
+    """Tiny CPU-checkable case.
+
+    Per layer Q [256, 4, 64], K and V [256, 2, 64] ~ N(0,1)/sqrt(64), drawn in the
+    order layer0 Q, K, V, then layer1 Q, K, V.  Router: x_Q [256, 256] ~ N(0,1),
+    W1 [16, 256] Xavier, b1 = 0, and logits fixed by W2 = 0, b2 = (+1, -1), which
+    sends layer 0 to FA and layer 1 to SA."""
+    c = TINY
+    rng = np.random.default_rng(seed)
+    s = 1.0 / math.sqrt(c["d"])
+    layers = []
+    for _ in range(c["n_layers"]):
+        q = normal(rng, (c["seq"], c["hq"], c["d"]), s)
+        k = normal(rng, (c["seq"], c["hkv"], c["d"]), s)
+        v = normal(rng, (c["seq"], c["hkv"], c["d"]), s)
+        layers.append((q, k, v))
+    x_q = normal(rng, (c["seq"], c["hidden"]))
+    w1 = xavier_uniform(rng, c["router_hidden"], c["hidden"])
+    b1 = np.zeros(c["router_hidden"], np.float32)
+    w2 = np.zeros((c["n_layers"], c["router_hidden"]), np.float32)
+    b2 = np.array([1.0, -1.0], np.float32)
+    cu = np.array([0, c["seq"]], np.int32)
+    return dict(cfg=c, layers=layers, x_q=x_q, w1=w1, b1=b1, w2=w2, b2=b2, cu_seqlens=cu)
+
+
+def router_weights(rng: np.random.Generator, hidden: int, router_hidden: int, n_layers: int):
+    """Random-init Xavier router MLP hidden -> router_hidden -> n_layers, zero biases."""
+    w1 = xavier_uniform(rng, router_hidden, hidden)
+    b1 = np.zeros(router_hidden, np.float32)
+    w2 = xavier_uniform(rng, n_layers, router_hidden)
+    b2 = np.zeros(n_layers, np.float32)
+    return w1, b1, w2, b2
+
+
+def cu_seqlens_of(lengths) -> np.ndarray:
+    cu = np.zeros(len(lengths) + 1, np.int32)
+    cu[1:] = np.cumsum(np.asarray(lengths, np.int64))
+    return cu
+
+
+def qkv_host(rng: np.random.Generator, total: int, hq: int, hkv: int, d: int,
+             scale: float = 1.0, bf16: bool = True):
+    """Packed Q [total, hq, d] and K, V [total, hkv, d] ~ N(0, scale^2).
+
+    bf16=True returns uint16 bit patterns (RNE from fp32), else fp32."""
+    q = normal(rng, (total, hq, d), scale)
+    k = normal(rng, (total, hkv, d), scale)
+    v = normal(rng, (total, hkv, d), scale)
+    if bf16:
+        return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+    return q, k, v
+
+
+def kv_cache_host(rng: np.random.Generator, batch: int, hkv: int, max_cache: int, d: int,
+                  scale: float = 1.0, bf16: bool = True):
+    """KV cache [batch, hkv, max_cache, d] ~ N(0, scale^2)."""
+    k = normal(rng, (batch, hkv, max_cache, d), scale)
+    v = normal(rng, (batch, hkv, max_cache, d), scale)
+    if bf16:
+        return f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+    return k, v
+
+
+# ---------------------------------------------------------------------------
+# Device-side generators for the large shapes (torch is plumbing only).
+# ---------------------------------------------------------------------------
+
+def device_normal(shape, seed: int, dtype_name: str = "bf16", device: str = "cuda:0",
+                  scale: float = 1.0):
+    """N(0, scale^2) tensor drawn on the device from a seeded torch.Generator."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    dt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if scale != 1.0:
+        t.mul_(scale)
+    return t.to(dt)
