@@ -1,0 +1,227 @@
+/*
+ * fluxattn.h -- C ABI of the MI355X (gfx950) layer-routed hybrid attention
+ * library (libfluxattn.so).
+ *
+ * Method: Flux Attention ("Flux Attention: Context-Aware Hybrid Attention for
+ * Efficient LLMs Inference").  A lightweight Layer Router reads the query
+ * hidden states x_Q and sends every layer to Full Attention (FA) or Sparse
+ * Attention (SA) [HF model card, summary paragraph; thelatestinai paper page,
+ * Figure 2].  The decision is made once at prefill and reused by decode
+ * [thelatestinai paper page, Table 3].  FA is dense causal GQA attention
+ * (FlashAttention-2 is the dense path of [thelatestinai paper page, Table 6]);
+ * SA is streaming block-sparse attention that keeps the attention-sink blocks
+ * plus a local window of blocks (block size / sink size of the same Table 6,
+ * and the streaming block-sparse helper named in the codewithpapers function
+ * list).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers, allocated and owned by the caller.
+ *     The library keeps no pointer after a call returns and allocates no
+ *     device memory; scratch space comes in through `workspace`.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues work on that stream and returns without
+ *     synchronising; results are ready when the stream reaches that point.
+ *   - Arguments are validated on the host before anything is enqueued.  On a
+ *     validation failure nothing is launched and the call returns
+ *     FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED / FA_ERR_WORKSPACE; a launch
+ *     failure returns FA_ERR_HIP.  fa_last_error() gives a message for the
+ *     calling thread's most recent failure.  Host-side checks cannot see
+ *     device-resident values (sequence lengths, cache lengths); their device
+ *     behaviour is stated per entry point.
+ *   - dtype: FA_F32 (float) or FA_BF16 (bfloat16 bits).  Attention math
+ *     accumulates in fp32 in both cases.  Router weights are always fp32.
+ *   - Route mask: uint8 route[batch][n_layers], 1 = FA, 0 = SA (any nonzero
+ *     value counts as FA).
+ *   - Sparse configuration (tokens): block_tokens in {16, 32, 64, 128};
+ *     sink_tokens >= 0 and window_tokens >= block_tokens, both multiples of
+ *     block_tokens.  With ns = sink/block and nw = window/block, a query at
+ *     position t (query block i = t / block) of an SA layer sees key s iff
+ *     s <= t and (s / block < ns or s / block >= i - nw + 1): the window counts
+ *     whole blocks including the query's own block.  FA layers see every
+ *     s <= t.  Positions restart at 0 in every sequence.
+ */
+#ifndef FLUXATTN_H
+#define FLUXATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1, /* bad shape, pointer, index or sparse config */
+    FA_ERR_UNSUPPORTED = 2, /* valid but not compiled: head_dim, dtype, GQA ratio */
+    FA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    FA_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+/* Message for the calling thread's most recent failure ("" if none).  The
+ * pointer stays valid until the next call on the same thread. */
+const char *fa_last_error(void);
+
+/* ABI version of this header (increments on any signature change). */
+int32_t fa_abi_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Layer Router                                                             */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Bytes of workspace fa_router_decide needs: (batch*hidden + batch*router_hidden)
+ * floats, rounded up to 256 B.
+ */
+size_t fa_router_workspace_size(int32_t batch, int32_t hidden,
+                                int32_t router_hidden);
+
+/*
+ * fa_router_decide -- Layer Router of [thelatestinai paper page, Figure 2]:
+ * one FA/SA bit per (sequence, layer) from the query hidden states.
+ *
+ *   p[b]  = mean of the last P = min(pool_tokens, T_b) rows of x_q[b]
+ *           (the suffix pooling budget of [thelatestinai paper page, Figure 8])
+ *   h     = ReLU(W1 p + b1)
+ *   logit = W2 h + b2
+ *   route[b][l] = logit > 0 ? 1 (FA) : 0 (SA)      (NaN -> SA)
+ *
+ * x_q      [total_tokens][hidden], fp32 or bf16 (x_dtype), packed varlen.
+ * cu_seqlens [batch+1] int32, device, prefix sums of the sequence lengths.
+ * w1 [router_hidden][hidden], b1 [router_hidden], w2 [n_layers][router_hidden],
+ *    b2 [n_layers]: fp32, device.
+ * route  [batch][n_layers] uint8 out; logits [batch][n_layers] fp32 out
+ *        (nullable).
+ * workspace: >= fa_router_workspace_size(batch, hidden, router_hidden) bytes.
+ * All sums are fp32 in a fixed order, so repeated calls are bitwise identical.
+ * Device behaviour: a sequence with T_b <= 0 gets route 0 and logits NaN.
+ * Errors: NULL required pointer, batch/hidden/router_hidden/n_layers <= 0,
+ * pool_tokens <= 0 -> FA_ERR_INVALID_ARG; bad x_dtype -> FA_ERR_UNSUPPORTED;
+ * small workspace -> FA_ERR_WORKSPACE.
+ */
+fa_status fa_router_decide(const void *x_q, int32_t x_dtype,
+                           const int32_t *cu_seqlens, int32_t batch,
+                           int32_t hidden, int32_t pool_tokens,
+                           const float *w1, const float *b1,
+                           int32_t router_hidden, const float *w2,
+                           const float *b2, int32_t n_layers, uint8_t *route,
+                           float *logits, void *workspace, size_t ws_bytes,
+                           void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Streaming block plan                                                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * fa_block_plan -- kept key blocks of every (sequence, query block) of one
+ * layer, the streaming block-sparse layout of [thelatestinai paper page,
+ * Table 6] (sink blocks + local window), exported for bit-exact checking.
+ * The attention kernels evaluate the same rule internally.
+ *
+ * plan [batch][max_qblocks][4] int32 out, ascending half-open block ranges
+ *   (0, sink_end, win_begin, i + 1):
+ *   FA: sink_end = win_begin = i + 1 (one range [0, i+1));
+ *   SA: sink_end = min(ns, i + 1), win_begin = max(sink_end, i - nw + 1).
+ *   Query blocks at or past ceil(T_b / block) get (0, 0, 0, 0).
+ * cu_seqlens [batch+1] int32 device; route [batch][n_layers] uint8 device.
+ * Errors: NULL pointer, batch/max_qblocks <= 0, layer outside [0, n_layers),
+ * bad sparse config -> FA_ERR_INVALID_ARG.
+ */
+fa_status fa_block_plan(const int32_t *cu_seqlens, int32_t batch,
+                        int32_t max_qblocks, const uint8_t *route,
+                        int32_t n_layers, int32_t layer, int32_t sink_tokens,
+                        int32_t window_tokens, int32_t block_tokens,
+                        int32_t *plan, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Prefill attention                                                        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * fa_attn_prefill -- causal attention of one layer over a packed varlen batch;
+ * each sequence runs FA or SA as its route bit for `layer` says.
+ *
+ *   O[t][h] = sum_s softmax_s(sm_scale * <Q[t][h], K[s][h/G]>) V[s][h/G]
+ *   over the visible keys s of the layer's kind; G = n_q_heads / n_kv_heads
+ *   (query heads h*G .. h*G+G-1 share KV head h, as `repeat_kv` does).
+ *   lse[t][h] = ln sum_s exp(sm_scale * <Q[t][h], K[s][h/G]>).
+ *
+ * q [total][n_q_heads][head_dim], k, v [total][n_kv_heads][head_dim] (dtype);
+ * o [total][n_q_heads][head_dim] out (dtype); lse [total][n_q_heads] fp32 out
+ * (nullable).  total = cu_seqlens[batch].
+ * max_seqlen: host upper bound of every T_b (sizes the grid; rows of a longer
+ * sequence past max_seqlen are not computed).
+ * Supported: head_dim 64 or 128, any G.  bf16 with G in {1, 2, 4, 8, 16}
+ * runs on the MFMA kernel; other bf16 G and all fp32 inputs run on a plain
+ * one-thread-per-row kernel (the fp32 correctness path).
+ * SA tiles outside the sink and window ranges are never loaded.
+ * Errors: NULL pointer, batch/max_seqlen <= 0, heads <= 0, n_q_heads %
+ * n_kv_heads != 0, layer outside [0, n_layers), sm_scale not finite or <= 0,
+ * bad sparse config -> FA_ERR_INVALID_ARG; other head_dim/dtype/G ->
+ * FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_attn_prefill(const void *q, const void *k, const void *v, void *o,
+                          float *lse, int32_t dtype, const int32_t *cu_seqlens,
+                          int32_t batch, int32_t max_seqlen, int32_t n_q_heads,
+                          int32_t n_kv_heads, int32_t head_dim,
+                          const uint8_t *route, int32_t n_layers,
+                          int32_t layer, int32_t sink_tokens,
+                          int32_t window_tokens, int32_t block_tokens,
+                          float sm_scale, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention                                                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Bytes of workspace fa_attn_decode needs for a cache of max_cache tokens
+ * (split-K partial outputs and log-sum-exps), rounded up to 256 B.
+ */
+size_t fa_decode_workspace_size(int32_t batch, int32_t n_q_heads,
+                                int32_t head_dim, int32_t max_cache);
+
+/*
+ * fa_attn_decode -- one decode step of one layer: a single new query token per
+ * sequence attends to its KV cache, reusing the prefill route bit
+ * [thelatestinai paper page, Table 3: prefill routing, decode reuse].  The
+ * query sits at absolute position n - 1, n = cache_len[b] (the cache length
+ * INCLUDING the new token); SA layers read only the sink and window blocks of
+ * query block (n - 1) / block.
+ *
+ * q [batch][n_q_heads][head_dim] (dtype); o [batch][n_q_heads][head_dim] out
+ * (dtype); lse [batch][n_q_heads] fp32 out (nullable).
+ * k_cache, v_cache [batch][n_kv_heads][max_cache][head_dim] (dtype).
+ * k_new, v_new [batch][n_kv_heads][head_dim] (nullable, both or neither): when
+ *   given, the new token's K/V are read from them and also written into the
+ *   cache at position n - 1; when NULL they must already be in the cache.
+ * cache_len [batch] int32 device.
+ * route [batch][n_layers] uint8 device; route_host (nullable) is a host copy
+ *   of the same mask: when given and every sequence is SA for `layer`, the
+ *   grid is sized to the sink + window span instead of max_cache.
+ * workspace >= fa_decode_workspace_size(batch, n_q_heads, head_dim, max_cache).
+ * The work is split over KV-token ranges; partial results are merged in a
+ * fixed order, so repeated calls are bitwise identical.
+ * Supported: head_dim 64 or 128, G = n_q_heads / n_kv_heads in [1, 16].
+ * Device behaviour: a sequence with cache_len outside [1, max_cache] touches
+ * no cache memory and gets NaN outputs.
+ * Errors: as fa_attn_prefill, plus max_cache <= 0, only one of k_new/v_new
+ * given -> FA_ERR_INVALID_ARG; small workspace -> FA_ERR_WORKSPACE.
+ */
+fa_status fa_attn_decode(const void *q, void *o, float *lse, const void *k_new,
+                         const void *v_new, void *k_cache, void *v_cache,
+                         int32_t max_cache, const int32_t *cache_len,
+                         int32_t dtype, int32_t batch, int32_t n_q_heads,
+                         int32_t n_kv_heads, int32_t head_dim,
+                         const uint8_t *route, const uint8_t *route_host,
+                         int32_t n_layers, int32_t layer, int32_t sink_tokens,
+                         int32_t window_tokens, int32_t block_tokens,
+                         float sm_scale, void *workspace, size_t ws_bytes,
+                         void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLUXATTN_H */

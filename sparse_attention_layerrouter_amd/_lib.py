@@ -1,0 +1,187 @@
+"""ctypes binding of libfluxattn.so (the C ABI in include/fluxattn.h).
+
+Argument marshalling only: every function below has the name of its C entry
+point, takes torch tensors (device memory owned by the caller), reads shapes
+off them, passes raw pointers and the current HIP stream, and raises
+FluxAttnError when the C call returns a non-OK status.  All arithmetic happens
+in the library's gfx950 kernels; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfluxattn.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
+FA_F32, FA_BF16 = 0, 1
+
+EXPORTS = (
+    "fa_last_error", "fa_abi_version", "fa_router_workspace_size", "fa_router_decide",
+    "fa_block_plan", "fa_attn_prefill", "fa_decode_workspace_size", "fa_attn_decode",
+)
+
+
+class FluxAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfluxattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m sparse_attention_layerrouter_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    L.fa_last_error.restype = ctypes.c_char_p
+    L.fa_last_error.argtypes = []
+    L.fa_abi_version.restype = I32
+    L.fa_abi_version.argtypes = []
+    L.fa_router_workspace_size.restype = SZ
+    L.fa_router_workspace_size.argtypes = [I32, I32, I32]
+    L.fa_router_decide.restype = I32
+    L.fa_router_decide.argtypes = [P, I32, P, I32, I32, I32, P, P, I32, P, P, I32, P, P, P, SZ, P]
+    L.fa_block_plan.restype = I32
+    L.fa_block_plan.argtypes = [P, I32, I32, P, I32, I32, I32, I32, I32, P, P]
+    L.fa_attn_prefill.restype = I32
+    L.fa_attn_prefill.argtypes = [P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, P, I32, I32,
+                                  I32, I32, I32, F, P]
+    L.fa_decode_workspace_size.restype = SZ
+    L.fa_decode_workspace_size.argtypes = [I32, I32, I32, I32]
+    L.fa_attn_decode.restype = I32
+    L.fa_attn_decode.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, P, P, I32,
+                                 I32, I32, I32, I32, F, P, SZ, P]
+    _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().fa_last_error().decode()
+
+
+def _check(status: int):
+    if status != FA_OK:
+        raise FluxAttnError(status, last_error())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return FA_F32
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libfluxattn works on device tensors only")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def fa_abi_version() -> int:
+    return int(lib().fa_abi_version())
+
+
+def fa_router_workspace_size(batch: int, hidden: int, router_hidden: int) -> int:
+    return int(lib().fa_router_workspace_size(batch, hidden, router_hidden))
+
+
+def fa_decode_workspace_size(batch: int, n_q_heads: int, head_dim: int, max_cache: int) -> int:
+    return int(lib().fa_decode_workspace_size(batch, n_q_heads, head_dim, max_cache))
+
+
+def fa_router_decide(x_q, cu_seqlens, pool_tokens, w1, b1, w2, b2, route, logits=None,
+                     workspace=None, stream=None):
+    """Layer Router: x_q [total, hidden] -> route [B, L] uint8 (1 = FA)."""
+    import torch
+    _require_cuda(x_q, cu_seqlens, w1, b1, w2, b2, route, logits)
+    batch = cu_seqlens.numel() - 1
+    hidden = x_q.shape[-1]
+    router_hidden, n_layers = w1.shape[0], w2.shape[0]
+    if workspace is None:
+        n = fa_router_workspace_size(batch, hidden, router_hidden)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=x_q.device)
+    _check(lib().fa_router_decide(
+        _ptr(x_q), _dtype_code(x_q), _ptr(cu_seqlens), batch, hidden, pool_tokens, _ptr(w1),
+        _ptr(b1), router_hidden, _ptr(w2), _ptr(b2), n_layers, _ptr(route), _ptr(logits),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def fa_block_plan(cu_seqlens, max_qblocks, route, layer, sink_tokens, window_tokens,
+                  block_tokens, plan, stream=None):
+    """Kept key-block ranges: plan [B, max_qblocks, 4] int32."""
+    _require_cuda(cu_seqlens, route, plan)
+    batch = cu_seqlens.numel() - 1
+    _check(lib().fa_block_plan(
+        _ptr(cu_seqlens), batch, max_qblocks, _ptr(route), route.shape[1], layer, sink_tokens,
+        window_tokens, block_tokens, _ptr(plan), _stream(stream)))
+
+
+def fa_attn_prefill(q, k, v, o, cu_seqlens, max_seqlen, route, layer, sink_tokens,
+                    window_tokens, block_tokens, sm_scale, lse=None, stream=None):
+    """Prefill attention of one layer: q [total, Hq, d], k/v [total, Hkv, d] -> o."""
+    _require_cuda(q, k, v, o, cu_seqlens, route, lse)
+    batch = cu_seqlens.numel() - 1
+    _, hq, d = q.shape
+    hkv = k.shape[1]
+    _check(lib().fa_attn_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dtype_code(q), _ptr(cu_seqlens), batch,
+        int(max_seqlen), hq, hkv, d, _ptr(route), route.shape[1], layer, sink_tokens,
+        window_tokens, block_tokens, float(sm_scale), _stream(stream)))
+
+
+def fa_attn_decode(q, o, k_cache, v_cache, cache_len, route, layer, sink_tokens, window_tokens,
+                   block_tokens, sm_scale, workspace=None, k_new=None, v_new=None, lse=None,
+                   route_host=None, stream=None):
+    """Decode step of one layer: q [B, Hq, d] over k/v_cache [B, Hkv, max_cache, d] -> o."""
+    import torch
+    _require_cuda(q, o, k_cache, v_cache, cache_len, route, k_new, v_new, lse)
+    batch, hq, d = q.shape
+    hkv, max_cache = k_cache.shape[1], k_cache.shape[2]
+    if workspace is None:
+        n = fa_decode_workspace_size(batch, hq, d, max_cache)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    rh = None
+    if route_host is not None:
+        rh = np.ascontiguousarray(np.asarray(route_host, dtype=np.uint8))
+    _check(lib().fa_attn_decode(
+        _ptr(q), _ptr(o), _ptr(lse), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        max_cache, _ptr(cache_len), _dtype_code(q), batch, hq, hkv, d, _ptr(route),
+        None if rh is None else rh.ctypes.data_as(ctypes.c_void_p), route.shape[1], layer,
+        sink_tokens, window_tokens, block_tokens, float(sm_scale), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -1,0 +1,288 @@
+// api.cpp -- the C ABI of libfluxattn (include/fluxattn.h): host-side argument
+// validation, workspace sizing and dispatch to the gfx950 launchers.
+//
+// Nothing here touches the GPU before validation has passed, so every error
+// path can be exercised on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "fa_launch.h"
+#include "fluxattn.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa_status fail(fa_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+fa_status ok()
+{
+    g_last_error.clear();
+    return FA_OK;
+}
+
+fa_status hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return ok();
+    return fail(FA_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+int ilog2_exact(int v)
+{
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return (1 << l) == v ? l : -1;
+}
+
+// Sparse configuration in tokens -> (ns, nw, log2 block); false if invalid.
+bool sparse_cfg(int sink, int window, int block, int &ns, int &nw, int &bk_log2)
+{
+    bk_log2 = ilog2_exact(block);
+    if (bk_log2 < 4 || bk_log2 > 7) return false;  // block in {16, 32, 64, 128}
+    if (sink < 0 || sink % block != 0) return false;
+    if (window < block || window % block != 0) return false;
+    ns = sink / block;
+    nw = window / block;
+    return true;
+}
+
+size_t decode_splits_cap(int max_cache)
+{
+    int s = fa::decode_n_splits(max_cache);
+    return (size_t)(s > 64 ? s : 64);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *fa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t fa_abi_version(void) { return 1; }
+
+size_t fa_router_workspace_size(int32_t batch, int32_t hidden, int32_t router_hidden)
+{
+    if (batch <= 0 || hidden <= 0 || router_hidden <= 0) return 0;
+    return round256((size_t)batch * hidden * sizeof(float)) +
+           round256((size_t)batch * router_hidden * sizeof(float));
+}
+
+fa_status fa_router_decide(const void *x_q, int32_t x_dtype, const int32_t *cu_seqlens,
+                           int32_t batch, int32_t hidden, int32_t pool_tokens, const float *w1,
+                           const float *b1, int32_t router_hidden, const float *w2,
+                           const float *b2, int32_t n_layers, uint8_t *route, float *logits,
+                           void *workspace, size_t ws_bytes, void *stream)
+{
+    if (!x_q || !cu_seqlens || !w1 || !b1 || !w2 || !b2 || !route)
+        return fail(FA_ERR_INVALID_ARG, "fa_router_decide: a required pointer is NULL");
+    if (batch <= 0 || hidden <= 0 || router_hidden <= 0 || n_layers <= 0 || pool_tokens <= 0)
+        return fail(FA_ERR_INVALID_ARG,
+                    "fa_router_decide: batch=%d hidden=%d router_hidden=%d n_layers=%d "
+                    "pool_tokens=%d must all be positive",
+                    batch, hidden, router_hidden, n_layers, pool_tokens);
+    if (x_dtype != FA_F32 && x_dtype != FA_BF16)
+        return fail(FA_ERR_UNSUPPORTED, "fa_router_decide: x_dtype %d is not FA_F32/FA_BF16",
+                    x_dtype);
+    const size_t need = fa_router_workspace_size(batch, hidden, router_hidden);
+    if (!workspace || ws_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "fa_router_decide: workspace %zu bytes, need %zu",
+                    workspace ? ws_bytes : (size_t)0, need);
+    fa::RouterArgs a{};
+    a.x_q = x_q;
+    a.x_bf16 = x_dtype == FA_BF16;
+    a.cu_seqlens = cu_seqlens;
+    a.batch = batch;
+    a.hidden = hidden;
+    a.pool_tokens = pool_tokens;
+    a.w1 = w1;
+    a.b1 = b1;
+    a.router_hidden = router_hidden;
+    a.w2 = w2;
+    a.b2 = b2;
+    a.n_layers = n_layers;
+    a.route = route;
+    a.logits = logits;
+    a.ws_pool = (float *)workspace;
+    a.ws_hidden = (float *)((char *)workspace + round256((size_t)batch * hidden * sizeof(float)));
+    return hip_status(fa::launch_router(a, (hipStream_t)stream), "fa_router_decide");
+}
+
+fa_status fa_block_plan(const int32_t *cu_seqlens, int32_t batch, int32_t max_qblocks,
+                        const uint8_t *route, int32_t n_layers, int32_t layer,
+                        int32_t sink_tokens, int32_t window_tokens, int32_t block_tokens,
+                        int32_t *plan, void *stream)
+{
+    if (!cu_seqlens || !route || !plan)
+        return fail(FA_ERR_INVALID_ARG, "fa_block_plan: a required pointer is NULL");
+    if (batch <= 0 || max_qblocks <= 0)
+        return fail(FA_ERR_INVALID_ARG, "fa_block_plan: batch=%d max_qblocks=%d must be positive",
+                    batch, max_qblocks);
+    if (n_layers <= 0 || layer < 0 || layer >= n_layers)
+        return fail(FA_ERR_INVALID_ARG, "fa_block_plan: layer %d outside [0, %d)", layer, n_layers);
+    fa::PlanArgs a{};
+    if (!sparse_cfg(sink_tokens, window_tokens, block_tokens, a.ns, a.nw, a.bk_log2))
+        return fail(FA_ERR_INVALID_ARG,
+                    "fa_block_plan: bad sparse config sink=%d window=%d block=%d", sink_tokens,
+                    window_tokens, block_tokens);
+    a.cu_seqlens = cu_seqlens;
+    a.batch = batch;
+    a.max_qblocks = max_qblocks;
+    a.route = route;
+    a.n_layers = n_layers;
+    a.layer = layer;
+    a.plan = plan;
+    return hip_status(fa::launch_block_plan(a, (hipStream_t)stream), "fa_block_plan");
+}
+
+fa_status fa_attn_prefill(const void *q, const void *k, const void *v, void *o, float *lse,
+                          int32_t dtype, const int32_t *cu_seqlens, int32_t batch,
+                          int32_t max_seqlen, int32_t n_q_heads, int32_t n_kv_heads,
+                          int32_t head_dim, const uint8_t *route, int32_t n_layers,
+                          int32_t layer, int32_t sink_tokens, int32_t window_tokens,
+                          int32_t block_tokens, float sm_scale, void *stream)
+{
+    if (!q || !k || !v || !o || !cu_seqlens || !route)
+        return fail(FA_ERR_INVALID_ARG, "fa_attn_prefill: a required pointer is NULL");
+    if (batch <= 0 || max_seqlen <= 0)
+        return fail(FA_ERR_INVALID_ARG, "fa_attn_prefill: batch=%d max_seqlen=%d must be positive",
+                    batch, max_seqlen);
+    if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0)
+        return fail(FA_ERR_INVALID_ARG,
+                    "fa_attn_prefill: n_q_heads=%d must be a positive multiple of n_kv_heads=%d",
+                    n_q_heads, n_kv_heads);
+    if (n_layers <= 0 || layer < 0 || layer >= n_layers)
+        return fail(FA_ERR_INVALID_ARG, "fa_attn_prefill: layer %d outside [0, %d)", layer,
+                    n_layers);
+    if (!std::isfinite(sm_scale) || sm_scale <= 0.0f)
+        return fail(FA_ERR_INVALID_ARG, "fa_attn_prefill: sm_scale must be finite and > 0");
+    fa::PrefillArgs a{};
+    if (!sparse_cfg(sink_tokens, window_tokens, block_tokens, a.ns, a.nw, a.bk_log2))
+        return fail(FA_ERR_INVALID_ARG,
+                    "fa_attn_prefill: bad sparse config sink=%d window=%d block=%d", sink_tokens,
+                    window_tokens, block_tokens);
+    if (dtype != FA_F32 && dtype != FA_BF16)
+        return fail(FA_ERR_UNSUPPORTED, "fa_attn_prefill: dtype %d is not FA_F32/FA_BF16", dtype);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(FA_ERR_UNSUPPORTED, "fa_attn_prefill: head_dim %d not in {64, 128}", head_dim);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.bf16 = dtype == FA_BF16;
+    a.cu_seqlens = cu_seqlens;
+    a.batch = batch;
+    a.max_seqlen = max_seqlen;
+    a.hq = n_q_heads;
+    a.hkv = n_kv_heads;
+    a.d = head_dim;
+    a.route = route;
+    a.n_layers = n_layers;
+    a.layer = layer;
+    a.sm_scale = sm_scale;
+    return hip_status(fa::launch_prefill(a, (hipStream_t)stream), "fa_attn_prefill");
+}
+
+size_t fa_decode_workspace_size(int32_t batch, int32_t n_q_heads, int32_t head_dim,
+                                int32_t max_cache)
+{
+    if (batch <= 0 || n_q_heads <= 0 || head_dim <= 0 || max_cache <= 0) return 0;
+    const size_t rows = (size_t)batch * n_q_heads * decode_splits_cap(max_cache);
+    return round256(rows * head_dim * sizeof(float)) + round256(rows * sizeof(float));
+}
+
+fa_status fa_attn_decode(const void *q, void *o, float *lse, const void *k_new, const void *v_new,
+                         void *k_cache, void *v_cache, int32_t max_cache,
+                         const int32_t *cache_len, int32_t dtype, int32_t batch,
+                         int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                         const uint8_t *route, const uint8_t *route_host, int32_t n_layers,
+                         int32_t layer, int32_t sink_tokens, int32_t window_tokens,
+                         int32_t block_tokens, float sm_scale, void *workspace, size_t ws_bytes,
+                         void *stream)
+{
+    if (!q || !o || !k_cache || !v_cache || !cache_len || !route)
+        return fail(FA_ERR_INVALID_ARG, "fa_attn_decode: a required pointer is NULL");
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return fail(FA_ERR_INVALID_ARG, "fa_attn_decode: give both k_new and v_new, or neither");
+    if (batch <= 0 || max_cache <= 0)
+        return fail(FA_ERR_INVALID_ARG, "fa_attn_decode: batch=%d max_cache=%d must be positive",
+                    batch, max_cache);
+    if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0)
+        return fail(FA_ERR_INVALID_ARG,
+                    "fa_attn_decode: n_q_heads=%d must be a positive multiple of n_kv_heads=%d",
+                    n_q_heads, n_kv_heads);
+    if (n_layers <= 0 || layer < 0 || layer >= n_layers)
+        return fail(FA_ERR_INVALID_ARG, "fa_attn_decode: layer %d outside [0, %d)", layer,
+                    n_layers);
+    if (!std::isfinite(sm_scale) || sm_scale <= 0.0f)
+        return fail(FA_ERR_INVALID_ARG, "fa_attn_decode: sm_scale must be finite and > 0");
+    fa::DecodeArgs a{};
+    if (!sparse_cfg(sink_tokens, window_tokens, block_tokens, a.ns, a.nw, a.bk_log2))
+        return fail(FA_ERR_INVALID_ARG,
+                    "fa_attn_decode: bad sparse config sink=%d window=%d block=%d", sink_tokens,
+                    window_tokens, block_tokens);
+    if (dtype != FA_F32 && dtype != FA_BF16)
+        return fail(FA_ERR_UNSUPPORTED, "fa_attn_decode: dtype %d is not FA_F32/FA_BF16", dtype);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(FA_ERR_UNSUPPORTED, "fa_attn_decode: head_dim %d not in {64, 128}", head_dim);
+    const int G = n_q_heads / n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+        return fail(FA_ERR_UNSUPPORTED, "fa_attn_decode: GQA ratio %d not in {1,2,4,8,16}", G);
+
+    // Grid sizing: kept tokens per sequence are at most max_cache, or at most
+    // sink + window when the host mirror says every sequence is SA here.
+    int max_kept = max_cache;
+    if (route_host) {
+        bool all_sa = true;
+        for (int b = 0; b < batch; ++b)
+            if (route_host[(size_t)b * n_layers + layer]) all_sa = false;
+        if (all_sa && sink_tokens + window_tokens < max_kept)
+            max_kept = sink_tokens + window_tokens;
+    }
+    a.split_tokens = fa::decode_split_tokens(max_kept);
+    a.n_splits = fa::decode_n_splits(max_kept);
+    const size_t rows = (size_t)batch * n_q_heads * a.n_splits;
+    const size_t o_bytes = round256(rows * head_dim * sizeof(float));
+    const size_t need = o_bytes + round256(rows * sizeof(float));
+    if (!workspace || ws_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "fa_attn_decode: workspace %zu bytes, need %zu",
+                    workspace ? ws_bytes : (size_t)0, need);
+    a.q = q;
+    a.o = o;
+    a.lse = lse;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.max_cache = max_cache;
+    a.cache_len = cache_len;
+    a.bf16 = dtype == FA_BF16;
+    a.batch = batch;
+    a.hq = n_q_heads;
+    a.hkv = n_kv_heads;
+    a.d = head_dim;
+    a.route = route;
+    a.n_layers = n_layers;
+    a.layer = layer;
+    a.sm_scale = sm_scale;
+    a.o_part = (float *)workspace;
+    a.lse_part = (float *)((char *)workspace + o_bytes);
+    return hip_status(fa::launch_decode(a, (hipStream_t)stream), "fa_attn_decode");
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// fa_launch.h -- host-side launchers of the gfx950 kernels (internal to
+// libfluxattn; the public surface is include/fluxattn.h).  Every launcher only
+// enqueues on `stream` and returns hipGetLastError() of the launch.  Arguments
+// are already validated by api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct RouterArgs {
+    const void *x_q;
+    int x_bf16;
+    const int32_t *cu_seqlens;
+    int batch, hidden, pool_tokens;
+    const float *w1, *b1;
+    int router_hidden;
+    const float *w2, *b2;
+    int n_layers;
+    uint8_t *route;
+    float *logits;
+    float *ws_pool;    // [batch][hidden]
+    float *ws_hidden;  // [batch][router_hidden]
+};
+hipError_t launch_router(const RouterArgs &a, hipStream_t stream);
+
+struct PlanArgs {
+    const int32_t *cu_seqlens;
+    int batch, max_qblocks;
+    const uint8_t *route;
+    int n_layers, layer;
+    int ns, nw, bk_log2;
+    int32_t *plan;
+};
+hipError_t launch_block_plan(const PlanArgs &a, hipStream_t stream);
+
+struct PrefillArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    int bf16;
+    const int32_t *cu_seqlens;
+    int batch, max_seqlen, hq, hkv, d;
+    const uint8_t *route;
+    int n_layers, layer;
+    int ns, nw, bk_log2;
+    float sm_scale;
+};
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+struct DecodeArgs {
+    const void *q;
+    void *o;
+    float *lse;
+    const void *k_new, *v_new;
+    void *k_cache, *v_cache;
+    int max_cache;
+    const int32_t *cache_len;
+    int bf16;
+    int batch, hq, hkv, d;
+    const uint8_t *route;
+    int n_layers, layer;
+    int ns, nw, bk_log2;
+    float sm_scale;
+    int split_tokens;  // KV tokens per split (multiple of 64)
+    int n_splits;      // splits launched per (sequence, kv head)
+    float *o_part;     // [batch][hq][n_splits][d]
+    float *lse_part;   // [batch][hq][n_splits]
+};
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+// Split policy shared by fa_decode_workspace_size and fa_attn_decode.
+int decode_split_tokens(int max_kept_tokens);
+inline int decode_n_splits(int max_kept_tokens)
+{
+    int st = decode_split_tokens(max_kept_tokens);
+    return (max_kept_tokens + st - 1) / st;
+}
+
+}  // namespace fa
