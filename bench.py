@@ -1,0 +1,418 @@
+#!/usr/bin/env python3
+"""Benchmark of the layer-routed hybrid attention hot path on one MI355X.
+
+One step = the whole hot path on one batch of synthetic, HBM-resident input:
+  1. Layer Router: x_Q [131072, 4096] bf16, mean of the last 64 rows, fp32 MLP
+     4096 -> 256 -> 32 (random Xavier), threshold -> 32 FA/SA bits;
+  2. prefill of a 131072-token sequence through 32 Llama-3.1-8B-shaped
+     attention layers (32 query / 8 KV heads, head_dim 128, bf16), each layer FA
+     or SA (sink 128, window 2048, block 64) by the router's bit;
+  3. one decode step of batch 8 over 32 layers with 131072-token bf16 KV caches
+     (even layers FA, odd layers SA, same sparse configuration).
+The prefill throughput of step 1+2 is `value` (tok/s at 128k); decode tok/s is
+reported beside it.  Inputs are N(0, 1) drawn on the device from fixed seeds.
+
+Prints ONE JSON line.  `--gpus` above 1 is refused: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+HQ, HKV, D = 32, 8, 128
+HIDDEN, ROUTER_HIDDEN, N_LAYERS, POOL = 4096, 256, 32, 64
+SINK, WINDOW, BLOCK = 128, 2048, 64
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=1)
+    p.add_argument("--seq", type=int, default=131072, help="prefill context length")
+    p.add_argument("--decode-len", type=int, default=131072, help="KV cache length in decode")
+    p.add_argument("--decode-batch", type=int, default=8)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=48,
+                   help="query rows of the FA layer the oracle times (SA gets 4x)")
+    p.add_argument("--profile", action="store_true",
+                   help="short kernel-only run for rocprofv3 counter passes")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (visible (q, k) pairs; bytes of visible K/V rows)
+# ---------------------------------------------------------------------------
+
+def pairs_fa(T: int) -> int:
+    return T * (T + 1) // 2
+
+
+def pairs_sa(T: int, sink=SINK, window=WINDOW, block=BLOCK) -> int:
+    """Visible pairs of one SA sequence: sum over rows of the kept-range sizes."""
+    ns, nw = sink // block, window // block
+    n = 0
+    nqb = -(-T // block)
+    for i in range(nqb):
+        rows = min(block, T - i * block)
+        # full kept blocks strictly before the diagonal block
+        if i < ns:
+            full = i
+        else:
+            full = ns + (i - max(ns, i - nw + 1))
+        # rows of block i see `full` whole blocks and 1..rows keys of their own block
+        n += rows * full * block + rows * (rows + 1) // 2
+    return n
+
+
+def flops_of_pairs(p: int) -> float:
+    return 4.0 * D * HQ * p  # QK^T and PV, 2 flop per MAC, all query heads
+
+
+def kept_tokens_decode(n: int, is_fa: bool, sink=SINK, window=WINDOW, block=BLOCK) -> int:
+    if is_fa:
+        return n
+    i = (n - 1) // block
+    sink_len = min(sink, n)
+    win_start = min(max(sink, (i - window // block + 1) * block), n)
+    return sink_len + n - win_start
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sparse_attention_layerrouter_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_key: str, src_hash: str):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = data.get(kernel_key)
+    if not e or e.get("source_hash") != src_hash:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def log(msg: str):
+    """Progress on stderr (the JSON result is the only stdout line)."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the routed attention step has no multi-GPU "
+              "path in this build (heads and sequences shard with no exchange; see the "
+              "design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_attention_layerrouter_amd import _lib, synth
+
+    _lib.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    T = args.seq
+    NB, NC = args.decode_batch, args.decode_len
+    if args.profile:
+        T, NC, n_dec_layers, n_sets = min(T, 32768), min(NC, 131072), 4, 2
+    else:
+        n_dec_layers, n_sets = N_LAYERS, 4
+    scale = 1.0 / math.sqrt(D)
+
+    # ---- inputs, resident in HBM before any timing -------------------------
+    x_q = synth.device_normal((T, HIDDEN), seed=11)
+    rng = np.random.default_rng(0)
+    w1, b1, w2, b2 = (torch.from_numpy(a).to(dev) for a in
+                      synth.router_weights(rng, HIDDEN, ROUTER_HIDDEN, N_LAYERS))
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    route = torch.zeros((1, N_LAYERS), dtype=torch.uint8, device=dev)
+    logits = torch.zeros((1, N_LAYERS), dtype=torch.float32, device=dev)
+    ws_router = torch.empty(_lib.fa_router_workspace_size(1, HIDDEN, ROUTER_HIDDEN),
+                            dtype=torch.uint8, device=dev)
+    sets = []
+    for s in range(n_sets):  # rotating per-layer Q/K/V sets, each far larger than the caches
+        sets.append((synth.device_normal((T, HQ, D), seed=100 + 3 * s),
+                     synth.device_normal((T, HKV, D), seed=101 + 3 * s),
+                     synth.device_normal((T, HKV, D), seed=102 + 3 * s)))
+    o_pre = torch.empty((T, HQ, D), dtype=torch.bfloat16, device=dev)
+
+    dec_route_np = np.array([[1 if l % 2 == 0 else 0 for l in range(N_LAYERS)]] * NB, np.uint8)
+    dec_route = torch.from_numpy(dec_route_np).to(dev)
+    caches = []
+    for l in range(n_dec_layers):  # one distinct cache per layer
+        kc = torch.empty((NB, HKV, NC, D), dtype=torch.bfloat16, device=dev)
+        vc = torch.empty_like(kc)
+        for b in range(NB):
+            kc[b] = synth.device_normal((HKV, NC, D), seed=1000 + 64 * l + 2 * b)
+            vc[b] = synth.device_normal((HKV, NC, D), seed=1001 + 64 * l + 2 * b)
+        caches.append((kc, vc))
+    q_dec = synth.device_normal((NB, HQ, D), seed=7)
+    o_dec = torch.empty_like(q_dec)
+    cache_len = torch.full((NB,), NC, dtype=torch.int32, device=dev)
+    ws_dec = torch.empty(_lib.fa_decode_workspace_size(NB, HQ, D, NC), dtype=torch.uint8,
+                         device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs resident: prefill T={T}, decode {n_dec_layers} layers x batch {NB} x {NC}")
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # ---- one step -----------------------------------------------------------
+    def step(rec=None, prefill_route=None):
+        e_r0, e_r1 = ev(), ev()
+        e_r0.record(stream)
+        _lib.fa_router_decide(x_q, cu, POOL, w1, b1, w2, b2, route, logits, ws_router)
+        e_r1.record(stream)
+        r = route if prefill_route is None else prefill_route
+        # the host learns the route once per request (decode reuses it as well); the
+        # copy lets each layer launch the kernel compiled for its kind
+        r_host = r.cpu().numpy()
+        pre = []
+        for l in range(N_LAYERS if not args.profile else 4):
+            q, k, v = sets[l % n_sets]
+            a, b_ = ev(), ev()
+            a.record(stream)
+            _lib.fa_attn_prefill(q, k, v, o_pre, cu, T, r, l, SINK, WINDOW, BLOCK, scale,
+                                 route_host=r_host)
+            b_.record(stream)
+            pre.append((a, b_))
+        dec = []
+        for l in range(n_dec_layers):
+            kc, vc = caches[l]
+            a, b_ = ev(), ev()
+            a.record(stream)
+            _lib.fa_attn_decode(q_dec, o_dec, kc, vc, cache_len, dec_route, l, SINK, WINDOW,
+                                BLOCK, scale, workspace=ws_dec, route_host=dec_route_np)
+            b_.record(stream)
+            dec.append((a, b_))
+        if rec is not None:
+            rec.append(((e_r0, e_r1), pre, dec))
+
+    if args.profile:
+        # kernel-only run for counter passes, plus a plain copy of known size
+        big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        big2 = torch.empty_like(big)
+        for _ in range(2):
+            step(prefill_route=torch.tensor([[1, 0, 1, 0] + [0] * 28], dtype=torch.uint8,
+                                            device=dev))
+            big2.copy_(big)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_run": True, "copy_bytes": big.numel()}))
+        return
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(recs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {wall:.2f} s")
+
+    route_np = route.cpu().numpy()[0]
+    logits_np = logits.cpu().numpy()[0]
+    n_fa = int(route_np.sum())
+
+    t_router = np.mean([a.elapsed_time(b) for (a, b), _, _ in recs]) * 1e-3
+    pre_t = np.array([[a.elapsed_time(b) * 1e-3 for a, b in pre] for _, pre, _ in recs])
+    dec_t = np.array([[a.elapsed_time(b) * 1e-3 for a, b in dec] for _, _, dec in recs])
+    t_prefill = t_router + pre_t.sum(axis=1).mean()
+    t_decode = dec_t.sum(axis=1).mean()
+    fa_layers = [l for l in range(N_LAYERS) if route_np[l]]
+    sa_layers = [l for l in range(N_LAYERS) if not route_np[l]]
+    t_fa = float(pre_t[:, fa_layers].mean()) if fa_layers else float("nan")
+    t_sa = float(pre_t[:, sa_layers].mean()) if sa_layers else float("nan")
+    dec_fa = [l for l in range(N_LAYERS) if dec_route_np[0, l]]
+    dec_sa = [l for l in range(N_LAYERS) if not dec_route_np[0, l]]
+    td_fa = float(dec_t[:, dec_fa].mean())
+    td_sa = float(dec_t[:, dec_sa].mean())
+
+    # measured all-FA references (one pass each, same events)
+    allfa = torch.ones((1, N_LAYERS), dtype=torch.uint8, device=dev)
+    ref = []
+    step(ref, prefill_route=allfa)
+    torch.cuda.synchronize()
+    (ra, rb), pre_ref, _ = ref[0]
+    t_prefill_allfa = ra.elapsed_time(rb) * 1e-3 + sum(a.elapsed_time(b) for a, b in pre_ref) * 1e-3
+    dec_allfa_route = torch.ones((NB, N_LAYERS), dtype=torch.uint8, device=dev)
+    a, b = ev(), ev()
+    a.record(stream)
+    for l in range(N_LAYERS):
+        kc, vc = caches[l]
+        _lib.fa_attn_decode(q_dec, o_dec, kc, vc, cache_len, dec_allfa_route, l, SINK, WINDOW,
+                            BLOCK, scale, workspace=ws_dec)
+    b.record(stream)
+    torch.cuda.synchronize()
+    t_decode_allfa = a.elapsed_time(b) * 1e-3
+
+    # ---- roofline --------------------------------------------------------------
+    fa_flop = flops_of_pairs(pairs_fa(T))
+    sa_flop = flops_of_pairs(pairs_sa(T))
+    achieved_tflops = fa_flop / t_fa / 1e12
+    pre_hash = source_hash("prefill.hip", "fa_common.h")
+    dec_hash = source_hash("decode.hip", "fa_common.h")
+    traffic_pre = read_traffic("prefill_bf16_fa_32k", pre_hash)
+    dec_bytes = NB * HKV * NC * D * 2 * 2 + 2 * NB * HQ * D * 2
+    dec_sa_bytes = NB * HKV * kept_tokens_decode(NC, False) * D * 2 * 2 + 2 * NB * HQ * D * 2
+    achieved_gbs = dec_bytes / td_fa / 1e9
+
+    result = {
+        "metric": "routed-attn prefill tok/s @128k + decode tok/s; % MFMA / HBM roofline",
+        "value": round(T / t_prefill, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1) on device, random-init Xavier router (no trained weights)",
+        "config": {
+            "workload": (f"Llama-3.1-8B-shaped attention (32 q / 8 kv heads, d 128): router "
+                         f"{HIDDEN}->{ROUTER_HIDDEN}->{N_LAYERS} + 32-layer routed prefill of "
+                         f"{T} tokens (SA: sink {SINK}, window {WINDOW}, block {BLOCK}) + "
+                         f"32-layer decode step, batch {NB}, {NC}-token cache, 16 SA layers"),
+            "seq_len": T, "global_batch": 1, "decode_batch": NB, "decode_cache": NC,
+            "parallelism": "single GPU",
+        },
+        "prefill": {
+            "tok_s": round(T / t_prefill, 1),
+            "ms": round(t_prefill * 1e3, 3),
+            "router_ms": round(t_router * 1e3, 4),
+            "n_fa_layers": n_fa, "omega_msr": round(1 - n_fa / N_LAYERS, 4),
+            "min_abs_logit": float(np.abs(logits_np).min()),
+            "fa_layer_ms": round(t_fa * 1e3, 3), "sa_layer_ms": round(t_sa * 1e3, 3),
+            "fa_layer_tflops": round(achieved_tflops, 1),
+            "sa_layer_tflops": round(sa_flop / t_sa / 1e12, 1) if sa_layers else None,
+            "all_fa_ms": round(t_prefill_allfa * 1e3, 3),
+            "speedup_vs_all_fa": round(t_prefill_allfa / t_prefill, 3),
+        },
+        "decode": {
+            "tok_s": round(NB / t_decode, 1),
+            "ms_per_token_step": round(t_decode * 1e3, 4),
+            "fa_layer_us": round(td_fa * 1e6, 2), "sa_layer_us": round(td_sa * 1e6, 2),
+            "fa_layer_gbs": round(achieved_gbs, 1),
+            "sa_layer_gbs": round(dec_sa_bytes / td_sa / 1e9, 1),
+            "all_fa_ms": round(t_decode_allfa * 1e3, 4),
+            "speedup_vs_all_fa": round(t_decode_allfa / t_decode, 3),
+        },
+        "roofline": {
+            "kernel": "prefill_bf16_kernel<128> (FA layer, 131072 tokens)",
+            "bound": "mfma", "achieved": round(achieved_tflops, 1),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_pre,
+        },
+        "roofline_decode": {
+            "kernel": "fa_attn_decode FA layer (split + merge kernels)",
+            "bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
+            "traffic": read_traffic("decode_bf16_fa_131k", dec_hash),
+        },
+    }
+
+    log("all-FA references done")
+    # ---- CPU oracle baseline (rank 0, N=1 only) and sampled parity -------------
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"], result["parity"] = cpu_baseline(
+            args, sets[0], route_np, T, scale, t_prefill)
+    print(json.dumps(result))
+
+
+def cpu_baseline(args, qkv, route_np, T, scale, t_prefill_gpu):
+    """Time the oracle on a bounded sample of the same prefill workload and scale it to
+    the metric's unit by visible-pair count.  Also compares the sampled GPU rows."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from sparse_attention_layerrouter_amd import _lib
+
+    q, k, v = qkv
+    dev = q.device
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    out = {}
+    errs = []
+    cores = os.cpu_count() or 1
+    samples = {}
+    for name, bit, n_rows in (("fa", 1, args.cpu_rows), ("sa", 0, 4 * args.cpu_rows)):
+        o = torch.empty_like(q)
+        _lib.fa_attn_prefill(q, k, v, o, cu, T,
+                             torch.tensor([[bit]], dtype=torch.uint8, device=dev), 0, SINK,
+                             WINDOW, BLOCK, scale, route_host=np.array([[bit]], np.uint8))
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(5 + bit)
+        rows = np.sort(rng.choice(T, size=n_rows, replace=False)).astype(np.int32)
+        qh = q.view(torch.int16).cpu().numpy().view(np.uint16)
+        kh = k.view(torch.int16).cpu().numpy().view(np.uint16)
+        vh = v.view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        o_ref, _ = oracle.attn_prefill(qh, kh, vh, [0, T], np.array([[bit]], np.uint8), 0,
+                                       SINK, WINDOW, BLOCK, scale, rows=rows, n_threads=cores)
+        dt = time.perf_counter() - t0
+        log(f"oracle {name}: {len(rows)} rows in {dt:.1f} s on {cores} threads")
+        # visible pairs of the sampled rows (per head)
+        if bit:
+            sp = int((rows + 1).sum())
+        else:
+            sp = 0
+            for t in rows:
+                i = t // BLOCK
+                full = i if i < SINK // BLOCK else SINK // BLOCK + (
+                    i - max(SINK // BLOCK, i - WINDOW // BLOCK + 1))
+                sp += full * BLOCK + (t - i * BLOCK + 1)
+        total_pairs = pairs_fa(T) if bit else pairs_sa(T)
+        samples[name] = (dt, sp, total_pairs, len(rows))
+        og = o[torch.from_numpy(rows.astype(np.int64)).to(dev)].float().cpu().numpy()
+        errs.append(float(np.abs(og - o_ref).max()))
+    n_fa = int(route_np.sum())
+    t_fa_cpu = samples["fa"][0] * samples["fa"][2] / samples["fa"][1]
+    t_sa_cpu = samples["sa"][0] * samples["sa"][2] / samples["sa"][1]
+    t_cpu = n_fa * t_fa_cpu + (N_LAYERS - n_fa) * t_sa_cpu
+    out = {
+        "value": round(T / t_cpu, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
+        "sample": (f"oracle (fp64, threads={cores}) on {samples['fa'][3]} random query rows x 32 "
+                   f"heads of one FA layer ({samples['fa'][0]:.1f} s) and {samples['sa'][3]} "
+                   f"rows of one SA layer ({samples['sa'][0]:.1f} s) at {T} tokens, scaled by "
+                   f"visible-pair count to the routed 32-layer prefill ({n_fa} FA layers); "
+                   f"router time ignored"),
+        "gpu_over_cpu": round(t_cpu / t_prefill_gpu, 1),
+    }
+    parity = {"sampled_rows_max_abs_err": max(errs), "tolerance": 2e-2,
+              "pass": max(errs) <= 2e-2}
+    return out, parity
+
+
+if __name__ == "__main__":
+    main()

@@ -153,6 +153,9 @@ fa_status fa_block_plan(const int32_t *cu_seqlens, int32_t batch,
  * (nullable).  total = cu_seqlens[batch].
  * max_seqlen: host upper bound of every T_b (sizes the grid; rows of a longer
  * sequence past max_seqlen are not computed).
+ * route [batch][n_layers] uint8 device; route_host (nullable) is a host copy of
+ *   the same mask: when every sequence has the same bit for `layer`, a kernel
+ *   compiled for that kind runs (identical results, no per-sequence branch).
  * Supported: head_dim 64 or 128, any G.  bf16 with G in {1, 2, 4, 8, 16}
  * runs on the MFMA kernel; other bf16 G and all fp32 inputs run on a plain
  * one-thread-per-row kernel (the fp32 correctness path).
@@ -166,8 +169,8 @@ fa_status fa_attn_prefill(const void *q, const void *k, const void *v, void *o,
                           float *lse, int32_t dtype, const int32_t *cu_seqlens,
                           int32_t batch, int32_t max_seqlen, int32_t n_q_heads,
                           int32_t n_kv_heads, int32_t head_dim,
-                          const uint8_t *route, int32_t n_layers,
-                          int32_t layer, int32_t sink_tokens,
+                          const uint8_t *route, const uint8_t *route_host,
+                          int32_t n_layers, int32_t layer, int32_t sink_tokens,
                           int32_t window_tokens, int32_t block_tokens,
                           float sm_scale, void *stream);
 
@@ -198,8 +201,9 @@ size_t fa_decode_workspace_size(int32_t batch, int32_t n_q_heads,
  *   cache at position n - 1; when NULL they must already be in the cache.
  * cache_len [batch] int32 device.
  * route [batch][n_layers] uint8 device; route_host (nullable) is a host copy
- *   of the same mask: when given and every sequence is SA for `layer`, the
- *   grid is sized to the sink + window span instead of max_cache.
+ *   of the same mask: when every sequence has the same bit for `layer`, a
+ *   kernel compiled for that kind runs, and for an all-SA layer the grid is
+ *   sized to the sink + window span instead of max_cache.
  * workspace >= fa_decode_workspace_size(batch, n_q_heads, head_dim, max_cache).
  * The work is split over KV-token ranges; partial results are merged in a
  * fixed order, so repeated calls are bitwise identical.

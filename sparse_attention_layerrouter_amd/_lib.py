@@ -55,8 +55,8 @@ def lib() -> ctypes.CDLL:
     L.fa_block_plan.restype = I32
     L.fa_block_plan.argtypes = [P, I32, I32, P, I32, I32, I32, I32, I32, P, P]
     L.fa_attn_prefill.restype = I32
-    L.fa_attn_prefill.argtypes = [P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, P, I32, I32,
-                                  I32, I32, I32, F, P]
+    L.fa_attn_prefill.argtypes = [P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, P, P, I32,
+                                  I32, I32, I32, I32, F, P]
     L.fa_decode_workspace_size.restype = SZ
     L.fa_decode_workspace_size.argtypes = [I32, I32, I32, I32]
     L.fa_attn_decode.restype = I32
@@ -152,17 +152,27 @@ def fa_block_plan(cu_seqlens, max_qblocks, route, layer, sink_tokens, window_tok
         window_tokens, block_tokens, _ptr(plan), _stream(stream)))
 
 
+def _host_u8(a):
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.uint8))
+    return arr, arr.ctypes.data_as(ctypes.c_void_p)
+
+
 def fa_attn_prefill(q, k, v, o, cu_seqlens, max_seqlen, route, layer, sink_tokens,
-                    window_tokens, block_tokens, sm_scale, lse=None, stream=None):
+                    window_tokens, block_tokens, sm_scale, lse=None, route_host=None,
+                    stream=None):
     """Prefill attention of one layer: q [total, Hq, d], k/v [total, Hkv, d] -> o."""
     _require_cuda(q, k, v, o, cu_seqlens, route, lse)
     batch = cu_seqlens.numel() - 1
     _, hq, d = q.shape
     hkv = k.shape[1]
+    keep, rh = _host_u8(route_host)
     _check(lib().fa_attn_prefill(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dtype_code(q), _ptr(cu_seqlens), batch,
-        int(max_seqlen), hq, hkv, d, _ptr(route), route.shape[1], layer, sink_tokens,
+        int(max_seqlen), hq, hkv, d, _ptr(route), rh, route.shape[1], layer, sink_tokens,
         window_tokens, block_tokens, float(sm_scale), _stream(stream)))
+    del keep
 
 
 def fa_attn_decode(q, o, k_cache, v_cache, cache_len, route, layer, sink_tokens, window_tokens,
@@ -176,12 +186,10 @@ def fa_attn_decode(q, o, k_cache, v_cache, cache_len, route, layer, sink_tokens,
     if workspace is None:
         n = fa_decode_workspace_size(batch, hq, d, max_cache)
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
-    rh = None
-    if route_host is not None:
-        rh = np.ascontiguousarray(np.asarray(route_host, dtype=np.uint8))
+    keep, rh = _host_u8(route_host)
     _check(lib().fa_attn_decode(
         _ptr(q), _ptr(o), _ptr(lse), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
-        max_cache, _ptr(cache_len), _dtype_code(q), batch, hq, hkv, d, _ptr(route),
-        None if rh is None else rh.ctypes.data_as(ctypes.c_void_p), route.shape[1], layer,
-        sink_tokens, window_tokens, block_tokens, float(sm_scale), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+        max_cache, _ptr(cache_len), _dtype_code(q), batch, hq, hkv, d, _ptr(route), rh,
+        route.shape[1], layer, sink_tokens, window_tokens, block_tokens, float(sm_scale),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    del keep

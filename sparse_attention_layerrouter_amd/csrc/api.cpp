@@ -61,6 +61,18 @@ bool sparse_cfg(int sink, int window, int block, int &ns, int &nw, int &bk_log2)
     return true;
 }
 
+// Route mode of one layer from the optional host copy of the mask.
+int route_mode(const uint8_t *route_host, int batch, int n_layers, int layer)
+{
+    if (!route_host) return fa::kModeMixed;
+    int n_fa = 0;
+    for (int b = 0; b < batch; ++b)
+        if (route_host[(size_t)b * n_layers + layer]) ++n_fa;
+    if (n_fa == batch) return fa::kModeFA;
+    if (n_fa == 0) return fa::kModeSA;
+    return fa::kModeMixed;
+}
+
 size_t decode_splits_cap(int max_cache)
 {
     int s = fa::decode_n_splits(max_cache);
@@ -73,7 +85,7 @@ extern "C" {
 
 const char *fa_last_error(void) { return g_last_error.c_str(); }
 
-int32_t fa_abi_version(void) { return 1; }
+int32_t fa_abi_version(void) { return 2; }
 
 size_t fa_router_workspace_size(int32_t batch, int32_t hidden, int32_t router_hidden)
 {
@@ -152,9 +164,10 @@ fa_status fa_block_plan(const int32_t *cu_seqlens, int32_t batch, int32_t max_qb
 fa_status fa_attn_prefill(const void *q, const void *k, const void *v, void *o, float *lse,
                           int32_t dtype, const int32_t *cu_seqlens, int32_t batch,
                           int32_t max_seqlen, int32_t n_q_heads, int32_t n_kv_heads,
-                          int32_t head_dim, const uint8_t *route, int32_t n_layers,
-                          int32_t layer, int32_t sink_tokens, int32_t window_tokens,
-                          int32_t block_tokens, float sm_scale, void *stream)
+                          int32_t head_dim, const uint8_t *route, const uint8_t *route_host,
+                          int32_t n_layers, int32_t layer, int32_t sink_tokens,
+                          int32_t window_tokens, int32_t block_tokens, float sm_scale,
+                          void *stream)
 {
     if (!q || !k || !v || !o || !cu_seqlens || !route)
         return fail(FA_ERR_INVALID_ARG, "fa_attn_prefill: a required pointer is NULL");
@@ -195,6 +208,7 @@ fa_status fa_attn_prefill(const void *q, const void *k, const void *v, void *o, 
     a.n_layers = n_layers;
     a.layer = layer;
     a.sm_scale = sm_scale;
+    a.mode = route_mode(route_host, batch, n_layers, layer);
     return hip_status(fa::launch_prefill(a, (hipStream_t)stream), "fa_attn_prefill");
 }
 
@@ -246,14 +260,10 @@ fa_status fa_attn_decode(const void *q, void *o, float *lse, const void *k_new, 
 
     // Grid sizing: kept tokens per sequence are at most max_cache, or at most
     // sink + window when the host mirror says every sequence is SA here.
+    a.mode = route_mode(route_host, batch, n_layers, layer);
     int max_kept = max_cache;
-    if (route_host) {
-        bool all_sa = true;
-        for (int b = 0; b < batch; ++b)
-            if (route_host[(size_t)b * n_layers + layer]) all_sa = false;
-        if (all_sa && sink_tokens + window_tokens < max_kept)
-            max_kept = sink_tokens + window_tokens;
-    }
+    if (a.mode == fa::kModeSA && sink_tokens + window_tokens < max_kept)
+        max_kept = sink_tokens + window_tokens;
     a.split_tokens = fa::decode_split_tokens(max_kept);
     a.n_splits = fa::decode_n_splits(max_kept);
     const size_t rows = (size_t)batch * n_q_heads * a.n_splits;

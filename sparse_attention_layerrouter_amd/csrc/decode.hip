@@ -58,7 +58,7 @@ __device__ __forceinline__ int phys_of(int v, int sink_len, int win_start)
     return v < sink_len ? v : win_start + (v - sink_len);
 }
 
-template <typename TE, int D, int G>
+template <typename TE, int D, int G, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const TE *__restrict__ q, const TE *__restrict__ k_new, const TE *__restrict__ v_new,
     TE *__restrict__ k_cache, TE *__restrict__ v_cache, int max_cache,
@@ -87,7 +87,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const int n = cache_len[b];
     if (n < 1 || n > max_cache) return;  // merge kernel writes NaN for this sequence
 
-    const bool is_fa = route[(size_t)b * n_layers + layer] != 0;
+    const bool is_fa = MODE == kModeFA ? true
+                       : MODE == kModeSA ? false
+                                         : route[(size_t)b * n_layers + layer] != 0;
     int sink_len, win_start;
     if (is_fa) {
         sink_len = n;
@@ -283,10 +285,17 @@ hipError_t launch_split(const DecodeArgs &a, hipStream_t stream, const SparseRul
                         float scale_log2)
 {
     dim3 grid(a.n_splits, a.batch * a.hkv);
-    decode_split_kernel<TE, D, G><<<grid, kThreads, 0, stream>>>(
-        (const TE *)a.q, (const TE *)a.k_new, (const TE *)a.v_new, (TE *)a.k_cache,
-        (TE *)a.v_cache, a.max_cache, a.cache_len, a.route, a.n_layers, a.layer, a.hq, a.hkv, r,
-        scale_log2, a.split_tokens, a.n_splits, a.o_part, a.lse_part);
+#define FA_DECODE_ARGS                                                                         \
+    (const TE *)a.q, (const TE *)a.k_new, (const TE *)a.v_new, (TE *)a.k_cache,                 \
+        (TE *)a.v_cache, a.max_cache, a.cache_len, a.route, a.n_layers, a.layer, a.hq, a.hkv, r, \
+        scale_log2, a.split_tokens, a.n_splits, a.o_part, a.lse_part
+    if (a.mode == kModeFA)
+        decode_split_kernel<TE, D, G, kModeFA><<<grid, kThreads, 0, stream>>>(FA_DECODE_ARGS);
+    else if (a.mode == kModeSA)
+        decode_split_kernel<TE, D, G, kModeSA><<<grid, kThreads, 0, stream>>>(FA_DECODE_ARGS);
+    else
+        decode_split_kernel<TE, D, G, kModeMixed><<<grid, kThreads, 0, stream>>>(FA_DECODE_ARGS);
+#undef FA_DECODE_ARGS
     return hipGetLastError();
 }
 

@@ -10,6 +10,12 @@
 
 namespace fa {
 
+// Route knowledge the host has for one layer: a host copy of the mask lets the
+// launcher pick a kernel compiled for all-FA or all-SA batches.
+constexpr int kModeMixed = 0;  // read each sequence's bit from the device mask
+constexpr int kModeFA = 1;     // every sequence is FA for this layer
+constexpr int kModeSA = 2;     // every sequence is SA for this layer
+
 struct RouterArgs {
     const void *x_q;
     int x_bf16;
@@ -47,6 +53,7 @@ struct PrefillArgs {
     int n_layers, layer;
     int ns, nw, bk_log2;
     float sm_scale;
+    int mode;  // kModeMixed / kModeFA / kModeSA
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
@@ -64,6 +71,7 @@ struct DecodeArgs {
     int n_layers, layer;
     int ns, nw, bk_log2;
     float sm_scale;
+    int mode;          // kModeMixed / kModeFA / kModeSA
     int split_tokens;  // KV tokens per split (multiple of 64)
     int n_splits;      // splits launched per (sequence, kv head)
     float *o_part;     // [batch][hq][n_splits][d]

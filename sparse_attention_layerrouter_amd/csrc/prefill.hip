@@ -130,7 +130,7 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const
 
 // One workgroup: 4 waves x 32 query rows.  Wave w handles head
 // h0 + w / WPH and positions p0 + (w % WPH) * 32 .. +32, WPH = 4 / HPW.
-template <int D>
+template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
@@ -166,7 +166,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const int p0 = ptile * bm_pos;
     if (p0 >= T) return;
     const int p1 = min(p0 + bm_pos, T);
-    const bool is_fa = route[(size_t)b * n_layers + layer] != 0;
+    const bool is_fa = MODE == kModeFA ? true
+                       : MODE == kModeSA ? false
+                                         : route[(size_t)b * n_layers + layer] != 0;
 
     const int h = kvh * G + hg * hpw + wave / wph;
     const int pw0 = p0 + (wave % wph) * 32;   // this wave's first position
@@ -329,7 +331,7 @@ __device__ __forceinline__ float ld_elem(const TE *p, int i)
         return ((const float *)p)[i];
 }
 
-template <typename TE, int D>
+template <typename TE, int D, int MODE>
 __global__ __launch_bounds__(64) void prefill_generic_kernel(
     const TE *__restrict__ q, const TE *__restrict__ k, const TE *__restrict__ v,
     TE *__restrict__ o, float *__restrict__ lse, const int32_t *__restrict__ cu,
@@ -344,7 +346,9 @@ __global__ __launch_bounds__(64) void prefill_generic_kernel(
     if (p0 >= T) return;
     const int p1 = min(p0 + 64, T);
     const int t = min(p0 + (int)threadIdx.x, T - 1);
-    const bool is_fa = route[(size_t)b * n_layers + layer] != 0;
+    const bool is_fa = MODE == kModeFA ? true
+                       : MODE == kModeSA ? false
+                                         : route[(size_t)b * n_layers + layer] != 0;
     const int G = hq / hkv;
     const int g = h / G;
 
@@ -390,18 +394,18 @@ __global__ __launch_bounds__(64) void prefill_generic_kernel(
     if (lse) lse[(size_t)(start + t) * hq + h] = (m + fast_log2(l)) * kLn2;
 }
 
-template <typename TE, int D>
+template <typename TE, int D, int MODE>
 hipError_t launch_generic(const PrefillArgs &a, hipStream_t stream, const SparseRule &r,
                           float scale_log2)
 {
     dim3 grid((a.max_seqlen + 63) / 64, a.hq, a.batch);
-    prefill_generic_kernel<TE, D><<<grid, 64, 0, stream>>>(
+    prefill_generic_kernel<TE, D, MODE><<<grid, 64, 0, stream>>>(
         (const TE *)a.q, (const TE *)a.k, (const TE *)a.v, (TE *)a.o, a.lse, a.cu_seqlens,
         a.route, a.n_layers, a.layer, a.hq, a.hkv, r, scale_log2);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, int MODE>
 hipError_t launch_mfma(const PrefillArgs &a, hipStream_t stream, const SparseRule &r,
                        float scale_log2)
 {
@@ -413,35 +417,46 @@ hipError_t launch_mfma(const PrefillArgs &a, hipStream_t stream, const SparseRul
     const int n_units = a.batch * a.hkv;
     const long long n_wg = (long long)n_ptiles * n_hgroups * n_units;
     if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    prefill_bf16_kernel<D><<<(unsigned)n_wg, kThreads, 0, stream>>>(
+    prefill_bf16_kernel<D, MODE><<<(unsigned)n_wg, kThreads, 0, stream>>>(
         (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, (uint16_t *)a.o,
         a.lse, a.cu_seqlens, a.route, a.n_layers, a.layer, a.hq, a.hkv, G, hpw, n_hgroups,
         n_units, n_ptiles, r, scale_log2);
     return hipGetLastError();
 }
 
-}  // namespace
-
 bool prefill_mfma_supported(int d, int G)
 {
     return (d == 128 || d == 64) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
 }
 
+template <int MODE>
+hipError_t launch_mode(const PrefillArgs &a, hipStream_t stream, const SparseRule &r,
+                       float scale_log2)
+{
+    const int G = a.hq / a.hkv;
+    if (a.bf16 && prefill_mfma_supported(a.d, G)) {
+        if (a.d == 128) return launch_mfma<128, MODE>(a, stream, r, scale_log2);
+        return launch_mfma<64, MODE>(a, stream, r, scale_log2);
+    }
+    if (a.bf16) {
+        if (a.d == 128) return launch_generic<uint16_t, 128, MODE>(a, stream, r, scale_log2);
+        return launch_generic<uint16_t, 64, MODE>(a, stream, r, scale_log2);
+    }
+    if (a.d == 128) return launch_generic<float, 128, MODE>(a, stream, r, scale_log2);
+    return launch_generic<float, 64, MODE>(a, stream, r, scale_log2);
+}
+
+}  // namespace
+
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream)
 {
     SparseRule r{a.ns, a.nw, a.bk_log2};
     const float scale_log2 = a.sm_scale * kLog2e;
-    const int G = a.hq / a.hkv;
-    if (a.bf16 && prefill_mfma_supported(a.d, G)) {
-        if (a.d == 128) return launch_mfma<128>(a, stream, r, scale_log2);
-        return launch_mfma<64>(a, stream, r, scale_log2);
+    switch (a.mode) {
+    case kModeFA: return launch_mode<kModeFA>(a, stream, r, scale_log2);
+    case kModeSA: return launch_mode<kModeSA>(a, stream, r, scale_log2);
+    default: return launch_mode<kModeMixed>(a, stream, r, scale_log2);
     }
-    if (a.bf16) {
-        if (a.d == 128) return launch_generic<uint16_t, 128>(a, stream, r, scale_log2);
-        return launch_generic<uint16_t, 64>(a, stream, r, scale_log2);
-    }
-    if (a.d == 128) return launch_generic<float, 128>(a, stream, r, scale_log2);
-    return launch_generic<float, 64>(a, stream, r, scale_log2);
 }
 
 }  // namespace fa

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_clean_error_state():
-    assert _lib.fa_abi_version() == 1
+    assert _lib.fa_abi_version() == 2
 
 
 def test_workspace_sizes():
@@ -51,12 +51,12 @@ def test_workspace_sizes():
 
 def prefill_args(**kw):
     a = dict(q=P, k=P, v=P, o=P, lse=None, dtype=1, cu=P, batch=1, max_seqlen=256, hq=32,
-             hkv=8, d=128, route=P, n_layers=2, layer=0, sink=128, window=2048, block=64,
-             scale=0.088, stream=None)
+             hkv=8, d=128, route=P, route_host=None, n_layers=2, layer=0, sink=128,
+             window=2048, block=64, scale=0.088, stream=None)
     a.update(kw)
     return [a[k] for k in ("q", "k", "v", "o", "lse", "dtype", "cu", "batch", "max_seqlen",
-                           "hq", "hkv", "d", "route", "n_layers", "layer", "sink", "window",
-                           "block", "scale", "stream")]
+                           "hq", "hkv", "d", "route", "route_host", "n_layers", "layer", "sink",
+                           "window", "block", "scale", "stream")]
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -376,3 +376,37 @@ def test_decode_llama_131k_sampled_heads():
             og = host_of(o[:, g * G:(g + 1) * G].contiguous())
             assert max_err(og, o_ref) <= TOL_BF16
             assert np.abs(lse[:, g * G:(g + 1) * G].cpu().numpy() - l_ref).max() <= TOL_LSE
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_route_host_kernels_match_device_route(bf16):
+    """A host copy of the mask selects kernels compiled for all-FA / all-SA layers;
+    their outputs must equal the device-route kernel bit for bit."""
+    rng = np.random.default_rng(77)
+    lengths = [400, 190]
+    cu = synth.cu_seqlens_of(lengths)
+    q, k, v = synth.qkv_host(rng, int(cu[-1]), 8, 2, 128, bf16=bf16)
+    qd, kd, vd, cud = dev_from(q), dev_from(k), dev_from(v), i32(cu)
+    for bit in (0, 1):
+        route = np.full((2, 1), bit, np.uint8)
+        outs = []
+        for rh in (None, route):
+            o = torch.empty_like(qd)
+            _lib.fa_attn_prefill(qd, kd, vd, o, cud, 400, u8(route), 0, 64, 128, 32, 0.09,
+                                 route_host=rh)
+            torch.cuda.synchronize()
+            outs.append(host_of(o))
+        assert np.array_equal(outs[0], outs[1])
+    rng = np.random.default_rng(78)
+    kc, vc = synth.kv_cache_host(rng, 2, 2, 3000, 128, bf16=bf16)
+    qq = synth.normal(rng, (2, 8, 128))
+    qq = synth.f32_to_bf16_bits(qq) if bf16 else qq
+    for bit in (0, 1):
+        route = np.full((2, 1), bit, np.uint8)
+        a = run_decode(qq, kc, vc, [3000, 2500], route, 0, 64, 256, 32, 0.09)
+        b = run_decode(qq, kc, vc, [3000, 2500], route, 0, 64, 256, 32, 0.09, route_host=route)
+        o_ref, _ = oracle.attn_decode(qq, kc, vc, [3000, 2500], route, 0, 64, 256, 32, 0.09)
+        tol = TOL_BF16 if bf16 else TOL_F32
+        assert max_err(a[0], o_ref) <= tol and max_err(b[0], o_ref) <= tol
+        if bit:  # same grid, same kernel body: identical bits
+            assert np.array_equal(a[0], b[0])
