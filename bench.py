@@ -45,10 +45,14 @@ def parse():
     p.add_argument("--decode-len", type=int, default=131072, help="KV cache length in decode")
     p.add_argument("--decode-batch", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=48,
+    p.add_argument("--cpu-rows", type=int, default=192,
                    help="query rows of the FA layer the oracle times (SA gets 4x)")
     p.add_argument("--profile", action="store_true",
-                   help="short kernel-only run for rocprofv3 counter passes")
+                   help="short kernel-only run for rocprofv3 counter passes: one FA and one "
+                        "SA prefill layer and one FA and one SA decode layer, twice")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only a plain 1 GiB read + 1 GiB write elementwise kernel (counter "
+                        "calibration)")
     return p.parse_args()
 
 
@@ -90,14 +94,6 @@ def kept_tokens_decode(n: int, is_fa: bool, sink=SINK, window=WINDOW, block=BLOC
     return sink_len + n - win_start
 
 
-def source_hash(*names) -> str:
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "sparse_attention_layerrouter_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def read_traffic(kernel_key: str, src_hash: str):
     """HBM traffic per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source; else None."""
@@ -132,15 +128,23 @@ def main():
     import torch
 
     from sparse_attention_layerrouter_amd import _lib, synth
+    from sparse_attention_layerrouter_amd.rocprof_summary import source_hash
 
     _lib.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        torch.mul(x, 1.0, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_each_way": x.numel() * 4}))
+        return
     stream = torch.cuda.current_stream()
     T = args.seq
     NB, NC = args.decode_batch, args.decode_len
     if args.profile:
-        T, NC, n_dec_layers, n_sets = min(T, 32768), min(NC, 131072), 4, 2
+        n_dec_layers, n_sets = 2, 2
     else:
         n_dec_layers, n_sets = N_LAYERS, 4
     scale = 1.0 / math.sqrt(D)
@@ -194,7 +198,7 @@ def main():
         # copy lets each layer launch the kernel compiled for its kind
         r_host = r.cpu().numpy()
         pre = []
-        for l in range(N_LAYERS if not args.profile else 4):
+        for l in range(N_LAYERS if not args.profile else 2):
             q, k, v = sets[l % n_sets]
             a, b_ = ev(), ev()
             a.record(stream)
@@ -215,15 +219,11 @@ def main():
             rec.append(((e_r0, e_r1), pre, dec))
 
     if args.profile:
-        # kernel-only run for counter passes, plus a plain copy of known size
-        big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        big2 = torch.empty_like(big)
+        # kernel-only run for counter passes: layer 0 FA, layer 1 SA (prefill and decode)
         for _ in range(2):
-            step(prefill_route=torch.tensor([[1, 0, 1, 0] + [0] * 28], dtype=torch.uint8,
-                                            device=dev))
-            big2.copy_(big)
+            step(prefill_route=torch.tensor([[1, 0] + [0] * 30], dtype=torch.uint8, device=dev))
         torch.cuda.synchronize()
-        print(json.dumps({"profile_run": True, "copy_bytes": big.numel()}))
+        print(json.dumps({"profile_run": True, "seq": T, "decode_cache": NC}))
         return
 
     for _ in range(args.warmup):

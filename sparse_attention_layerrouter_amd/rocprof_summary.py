@@ -1,0 +1,110 @@
+"""Condense rocprofv3 CSV output into the short summaries kept under profiles/.
+
+    python -m sparse_attention_layerrouter_amd.rocprof_summary stats DIR
+        per-kernel launch count and average / min / max duration from the
+        *kernel_stats.csv (and *kernel_trace.csv) files rocprofv3 wrote in DIR.
+    python -m sparse_attention_layerrouter_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR \\
+            COPY_FETCH_DIR COPY_WRITE_DIR OUT_JSON
+        HBM bytes per launch of the hot kernels from FETCH_SIZE / WRITE_SIZE
+        passes (KiB per dispatch), each scaled by what the same counter reads
+        for a plain 1 GiB read + 1 GiB write elementwise kernel.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+
+# kernels whose traffic the benchmark reports, by a substring of the demangled name
+HOT_KERNELS = {
+    "prefill_bf16_fa_131k": ("prefill_bf16_kernel<128, 1>", ("prefill.hip", "fa_common.h")),
+    "prefill_bf16_sa_131k": ("prefill_bf16_kernel<128, 2>", ("prefill.hip", "fa_common.h")),
+    "decode_bf16_fa_131k": ("decode_split_kernel<unsigned short, 128, 4, 1>",
+                            ("decode.hip", "fa_common.h")),
+    "decode_bf16_sa_131k": ("decode_split_kernel<unsigned short, 128, 4, 2>",
+                            ("decode.hip", "fa_common.h")),
+}
+COPY_BYTES = 1 << 30
+
+
+def source_hash(*names) -> str:
+    """Hash of kernel sources, so stale counter data can be recognised."""
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(PKG, "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _rows(directory, suffix):
+    out = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            out.extend(csv.DictReader(f))
+    return out
+
+
+def stats(directory):
+    rows = _rows(directory, "kernel_stats.csv")
+    if not rows:
+        raise SystemExit(f"no kernel_stats.csv under {directory}")
+    lines = [f"{'calls':>6} {'avg_us':>11} {'min_us':>11} {'max_us':>11} {'total_%':>8}  kernel"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"{int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>11.2f} "
+                     f"{float(r['MinNs']) / 1e3:>11.2f} {float(r['MaxNs']) / 1e3:>11.2f} "
+                     f"{float(r['Percentage']):>8.2f}  {r['Name'][:150]}")
+    return "\n".join(lines)
+
+
+def _counter_avg(directory, counter):
+    """{kernel name: average counter value per dispatch}."""
+    acc = {}
+    for r in _rows(directory, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        name = r["Kernel_Name"]
+        acc.setdefault(name, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def _largest(d):
+    return max(d.items(), key=lambda kv: kv[1])
+
+
+def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_json):
+    fetch = _counter_avg(fetch_dir, "FETCH_SIZE")
+    write = _counter_avg(write_dir, "WRITE_SIZE")
+    copy_name, copy_fetch = _largest(_counter_avg(copy_fetch_dir, "FETCH_SIZE"))
+    _, copy_write = _largest(_counter_avg(copy_write_dir, "WRITE_SIZE"))
+    f_scale = COPY_BYTES / (copy_fetch * 1024.0)
+    w_scale = COPY_BYTES / (copy_write * 1024.0)
+    out = {"_calibration": {"copy_kernel": copy_name[:120], "copy_bytes_each_way": COPY_BYTES,
+                            "fetch_kib": copy_fetch, "write_kib": copy_write,
+                            "fetch_scale": f_scale, "write_scale": w_scale}}
+    for key, (needle, srcs) in HOT_KERNELS.items():
+        fk = [v for k, v in fetch.items() if needle in k]
+        wk = [v for k, v in write.items() if needle in k]
+        if not fk or not wk:
+            continue
+        fb = fk[0] * 1024.0 * f_scale
+        wb = wk[0] * 1024.0 * w_scale
+        out[key] = {"kernel": needle, "fetch_bytes": fb, "write_bytes": wb,
+                    "bytes_per_launch": fb + wb, "source_hash": source_hash(*srcs)}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
+if __name__ == "__main__":
+    if len(sys.argv) >= 3 and sys.argv[1] == "stats":
+        print(stats(sys.argv[2]))
+    elif len(sys.argv) == 7 and sys.argv[1] == "traffic":
+        print(json.dumps(traffic(*sys.argv[2:7]), indent=1))
+    else:
+        print(__doc__)
+        sys.exit(2)
