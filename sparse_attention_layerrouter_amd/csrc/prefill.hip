@@ -31,95 +31,58 @@ namespace {
 
 constexpr int kBN = 64;        // keys per KV tile
 constexpr int kThreads = 256;  // 4 wavefronts
+constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 // ---------------------------------------------------------------------------
-// LDS layouts
+// LDS layout
 // ---------------------------------------------------------------------------
-// K tile: [64 keys][D] bf16, row stride D*2 bytes, 16-byte chunk c of key r
-// stored at chunk c ^ (r % (D/8)).
+// Each K or V tile is [64 keys][D] bf16, row-major (D*2 bytes per row), and is
+// written straight from global memory by global_load_lds_dwordx4: wave
+// instruction i fills 1 KiB, lane l's 16 bytes landing at byte 16*l, i.e. row
+// l / (D/8), chunk l % (D/8).  The lane chooses WHICH global chunk it fetches,
+// so the tile can be stored swizzled: physical chunk c of row r holds logical
+// chunk c ^ f(r).
+//   K, read by ds_read_b128 with 16 rows per bank sweep at one logical chunk:
+//     fK(r) = r % (D/8)  -> the 16 rows hit 16 distinct chunks.
+//   V, read by ds_read_b64_tr_b16 with 4 rows x 32 bytes per 16-lane group:
+//     fV(r) = 4 (r % 4)  -> the 4 rows of a group land in disjoint chunk pairs.
 template <int D>
-__device__ __forceinline__ int k_lds_off(int key, int chunk)
+__device__ __forceinline__ int swz_k(int r) { return r & (D / 8 - 1); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return (4 * (r & 3)) & (D / 8 - 1); }
+
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int chunk, int swz)
 {
-    constexpr int CH = D / 8;
-    return key * (D * 2) + ((chunk ^ (key & (CH - 1))) << 4);
-}
-// V^T tile: [D][64 keys] bf16, row stride 128 bytes, 8-byte slot s (4 keys) of
-// row d stored at slot s ^ g(d), g(d) = (d % 16) ^ ((d / 8) % 16).
-__device__ __forceinline__ int vt_lds_off(int d, int slot)
-{
-    int g = (d & 15) ^ ((d >> 3) & 15);
-    return d * 128 + ((slot ^ g) << 3);
+    return row * (D * 2) + ((chunk ^ swz) << 4);
 }
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------
-template <int D>
-struct TileRegs {
-    // K: D/32 passes of one 16-byte chunk; V: D/32 passes of 4 keys x 8 d
-    u32x4 k[D / 32];
-    u32x4 v[4];
-};
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
 
+// Asynchronous global -> LDS copy of key rows [k0, k0 + 64) of one KV head
+// (rows past the sequence end are clamped to T - 1: they are always masked).
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D> &r, const uint16_t *__restrict__ kb,
-                                          const uint16_t *__restrict__ vb, size_t row_stride,
-                                          int k0, int T, int tid)
+__device__ __forceinline__ void issue_tile(char *k_dst, char *v_dst, const uint16_t *__restrict__ kb,
+                                           const uint16_t *__restrict__ vb, size_t row_stride,
+                                           int k0, int T, int wave, int lane)
 {
-    constexpr int CH = D / 8;            // 16-byte chunks per row
-    constexpr int RPP = kThreads / CH;   // rows per pass
+    constexpr int CH = D / 8;              // 16-byte chunks per row
+    constexpr int RPI = 64 / CH;           // rows per wave instruction (1 KiB)
+    constexpr int NI = kBN / (RPI * 4);    // instructions per wave per tensor
+    const int c = lane % CH;
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-        int key = tid / CH + RPP * i;
-        int c = tid % CH;
-        int s = k0 + key;
-        if (s < T)
-            r.k[i] = *(const u32x4 *)(kb + (size_t)s * row_stride + c * 8);
-        else
-            r.k[i] = u32x4{0, 0, 0, 0};
-    }
-    // V: unit = (4 keys, 8 d); D/8 * 16 units; threads past the unit count idle.
-    constexpr int UNITS = CH * 16;
-    if (tid < UNITS) {
-        int c = tid % CH, kg = tid / CH;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int s = k0 + kg * 4 + j;
-            if (s < T)
-                r.v[j] = *(const u32x4 *)(vb + (size_t)s * row_stride + c * 8);
-            else
-                r.v[j] = u32x4{0, 0, 0, 0};
-        }
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D> &r, char *k_lds, char *vt_lds, int tid)
-{
-    constexpr int CH = D / 8;
-    constexpr int RPP = kThreads / CH;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-        int key = tid / CH + RPP * i;
-        int c = tid % CH;
-        *(u32x4 *)(k_lds + k_lds_off<D>(key, c)) = r.k[i];
-    }
-    constexpr int UNITS = CH * 16;
-    if (tid < UNITS) {
-        int c = tid % CH, kg = tid / CH;
-        // r.v[j] holds key kg*4+j, d = 8c .. 8c+7 (two bf16 per dword).
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            // d = 8c + 2w (low halves) and 8c + 2w + 1 (high halves)
-            uint32_t a0 = r.v[0][w], a1 = r.v[1][w], a2 = r.v[2][w], a3 = r.v[3][w];
-            uint32_t lo01 = __builtin_amdgcn_perm(a1, a0, 0x05040100);
-            uint32_t lo23 = __builtin_amdgcn_perm(a3, a2, 0x05040100);
-            uint32_t hi01 = __builtin_amdgcn_perm(a1, a0, 0x07060302);
-            uint32_t hi23 = __builtin_amdgcn_perm(a3, a2, 0x07060302);
-            int d0 = 8 * c + 2 * w;
-            *(u32x2 *)(vt_lds + vt_lds_off(d0, kg)) = u32x2{lo01, lo23};
-            *(u32x2 *)(vt_lds + vt_lds_off(d0 + 1, kg)) = u32x2{hi01, hi23};
-        }
+    for (int i = 0; i < NI; ++i) {
+        const int blk = wave * NI + i;     // 1 KiB block of the tile (wave-uniform)
+        const int row = blk * RPI + lane / CH;
+        const int s = min(k0 + row, T - 1);
+        const uint16_t *ks = kb + (size_t)s * row_stride + ((c ^ swz_k<D>(row)) << 3);
+        const uint16_t *vs = vb + (size_t)s * row_stride + ((c ^ swz_v<D>(row)) << 3);
+        __builtin_amdgcn_global_load_lds((const void *)ks, (lds_void *)(k_dst + blk * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)vs, (lds_void *)(v_dst + blk * 1024), 16, 0, 0);
     }
 }
 
@@ -138,8 +101,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     int hq, int hkv, int G, int hpw, int n_hgroups, int n_units, int n_ptiles,
     SparseRule rule, float scale_log2)
 {
-    __shared__ __attribute__((aligned(16))) char k_lds[kBN * D * 2];
-    __shared__ __attribute__((aligned(16))) char vt_lds[D * kBN * 2];
+    constexpr int TILE_BYTES = kBN * D * 2;
+    // [buffer][K, V] tiles, double-buffered
+    __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * TILE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -175,16 +139,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const bool wave_active = pw0 < T;
     const int pw_last = min(pw0 + 31, T - 1);  // last valid position of the wave
 
-    // ---- Q^T operand in registers: lane holds row pw0 + l32, d = ks*16 + half*8 ..
-    bf16x8 qreg[D / 16];
-    {
-        int t = min(pw0 + l32, T - 1);
-        const uint16_t *qr = q + ((size_t)(start + t) * hq + h) * D;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            qreg[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qr + ks * 16 + half * 8));
-    }
-
     // ---- KV tile schedule: [0, nA) then [tB0, tB0 + nB)
     int a_end, b_begin;
     kept_ranges(p0, p1, is_fa, rule, a_end, b_begin);
@@ -197,6 +151,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const size_t row_stride = (size_t)hkv * D;
     const uint16_t *kb = k + ((size_t)start * hkv + kvh) * D;
     const uint16_t *vb = v + ((size_t)start * hkv + kvh) * D;
+    issue_tile<D>(lds, lds + TILE_BYTES, kb, vb, row_stride, 0, T, wave, lane);
+
+    // ---- Q^T operand in registers: lane holds row pw0 + l32, d = ks*16 + half*8 ..
+    bf16x8 qreg[D / 16];
+    {
+        int t = min(pw0 + l32, T - 1);
+        const uint16_t *qr = q + ((size_t)(start + t) * hq + h) * D;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            qreg[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qr + ks * 16 + half * 8));
+    }
 
     // masking thresholds for this wave
     const int sink_tok = rule.ns << rule.bk_log2;
@@ -204,24 +169,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const int my_t = min(pw0 + l32, T - 1);  // query position of this lane's row
     const int my_win_lo = ((my_t >> rule.bk_log2) - rule.nw + 1) << rule.bk_log2;
 
+    // transposed V reads: lane (group g, a = (l%16)/4, bq = l%4) points at key row
+    // K0 + a, d columns C0 + 4 bq .. +3; the instruction hands lane l the 4 keys
+    // K0 .. K0+3 at d = C0 + l%16.
+    const int tr_a = (lane & 15) >> 2;
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-    float m_run = -INFINITY;  // running max, log2 domain
+    float m_run = -INFINITY;  // reference max, log2 domain
     float l_run = 0.0f;       // this lane's share of the row sum
-
-    TileRegs<D> regs;
-    if (n_tiles > 0) load_tile<D>(regs, kb, vb, row_stride, 0 * kBN, T, tid);
 
     for (int it = 0; it < n_tiles; ++it) {
         const int kt = it < nA ? it : tB0 + (it - nA);
         const int k0 = kt * kBN;
-        __syncthreads();  // previous tile fully consumed
-        store_tile<D>(regs, k_lds, vt_lds, tid);
-        __syncthreads();
+        const char *k_lds = lds + (it & 1) * 2 * TILE_BYTES;
+        const char *v_lds = k_lds + TILE_BYTES;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // tile `it` landed; the other buffer is free again
         if (it + 1 < n_tiles) {
             const int kn = (it + 1) < nA ? it + 1 : tB0 + (it + 1 - nA);
-            load_tile<D>(regs, kb, vb, row_stride, kn * kBN, T, tid);
+            char *nk = lds + ((it + 1) & 1) * 2 * TILE_BYTES;
+            issue_tile<D>(nk, nk + TILE_BYTES, kb, vb, row_stride, kn * kBN, T, wave, lane);
         }
         if (!wave_active || k0 > pw_last) continue;  // nothing visible for this wave
 
@@ -233,9 +203,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
         for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2) {
-                int key = kb2 * 32 + l32;
+                const int key = kb2 * 32 + l32;
                 bf16x8 a = __builtin_bit_cast(
-                    bf16x8, *(const u32x4 *)(k_lds + k_lds_off<D>(key, ks * 2 + half)));
+                    bf16x8, *(const u32x4 *)(k_lds + tile_off<D>(key, ks * 2 + half, swz_k<D>(key))));
                 s[kb2] = mfma32(a, qreg[ks], s[kb2]);
             }
         }
@@ -255,16 +225,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
                 }
         }
 
-        // ---- online softmax (exp2 domain)
+        // ---- online softmax (exp2 domain) with a lazily moved reference max:
+        // the reference m_ref only moves when a row's tile max exceeds it by more
+        // than kRescaleSlack (log2 units), so p = 2^(s - m_ref) <= 2^kRescaleSlack
+        // and the O / l rescale runs on few tiles.  O / l is independent of the
+        // reference, so the result is the same softmax.
         float mx = -INFINITY;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
             for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb2][j]);
-        mx = max_xor32(mx);
-        const float m_new = fmaxf(m_run, mx * scale_log2);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
+        mx = max_xor32(mx) * scale_log2;
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.0f : m_new));
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
         float psum = 0.0f;
         uint32_t pk[2][8];
 #pragma unroll
@@ -276,23 +256,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
                 psum += e0 + e1;
                 pk[kb2][j / 2] = pack_bf16x2(e0, e1);
             }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+        l_run += psum;
 
-        // ---- O^T += V^T P^T : 4 k-steps of 16 keys
+        // ---- O^T += V^T P^T : 4 k-steps of 16 keys.  P^T for k-step ksv is the
+        // lane's own S^T values 8*(ksv%2) .. +8 of block ksv/2: k index
+        // 8*half + e <-> key 16*ksv + 8*(e/4) + 4*half + e%4.
 #pragma unroll
         for (int ksv = 0; ksv < 4; ++ksv) {
             const int kb2 = ksv >> 1, jb = (ksv & 1) * 4;
             u32x4 pw = {pk[kb2][jb], pk[kb2][jb + 1], pk[kb2][jb + 2], pk[kb2][jb + 3]};
             bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+            const int r0 = 16 * ksv + 4 * half + tr_a;  // key row of this lane's pointer
+            const int r1 = r0 + 8;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
-                int d = dt * 32 + l32;
-                u32x2 lo = *(const u32x2 *)(vt_lds + vt_lds_off(d, 4 * ksv + half));
-                u32x2 hi = *(const u32x2 *)(vt_lds + vt_lds_off(d, 4 * ksv + 2 + half));
-                u32x4 aw = {lo[0], lo[1], hi[0], hi[1]};
+                const int col = dt * 32 + tr_col;   // d column of this lane's pointer
+                const int off_lo = tile_off<D>(r0, col >> 3, swz_v<D>(r0)) + (col & 7) * 2;
+                const int off_hi = tile_off<D>(r1, col >> 3, swz_v<D>(r1)) + (col & 7) * 2;
+                i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(v_lds + off_lo));
+                i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(v_lds + off_hi));
+                u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+                u32x4 aw = {lo2[0], lo2[1], hi2[0], hi2[1]};
                 oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, aw), pb, oacc[dt]);
             }
         }
