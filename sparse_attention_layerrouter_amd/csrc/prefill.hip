@@ -63,28 +63,63 @@ __device__ __forceinline__ int tile_off(int row, int chunk, int swz)
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 
-// Asynchronous global -> LDS copy of key rows [k0, k0 + 64) of one KV head
-// (rows past the sequence end are clamped to T - 1: they are always masked).
+// Asynchronous global -> LDS copies of one 64-key K tile and V tile.  Wave
+// instruction i of wave w fills 1 KiB block (w * NI + i) of a tile: lane l lands
+// at row (block * RPI + l / CH), chunk l % CH, and fetches the logical chunk the
+// swizzle stores there.  The per-lane byte offsets inside a full tile are fixed,
+// so they are computed once; only the tile base moves (a scalar).
 template <int D>
-__device__ __forceinline__ void issue_tile(char *k_dst, char *v_dst, const uint16_t *__restrict__ kb,
-                                           const uint16_t *__restrict__ vb, size_t row_stride,
-                                           int k0, int T, int wave, int lane)
-{
-    constexpr int CH = D / 8;              // 16-byte chunks per row
-    constexpr int RPI = 64 / CH;           // rows per wave instruction (1 KiB)
-    constexpr int NI = kBN / (RPI * 4);    // instructions per wave per tensor
-    const int c = lane % CH;
+struct TileLoader {
+    static constexpr int CH = D / 8;              // 16-byte chunks per row
+    static constexpr int RPI = 64 / CH;           // rows per wave instruction (1 KiB)
+    static constexpr int NI = kBN / (RPI * 4);    // instructions per wave per tensor
+    uint32_t off_k[NI], off_v[NI];                // byte offsets inside a full tile
+    int row[NI];                                  // tile row of each instruction
+    int lds_blk;                                  // first 1 KiB block of this wave
+    uint32_t chunk_k[NI], chunk_v[NI];
+
+    __device__ __forceinline__ void init(int wave, int lane, size_t row_stride)
+    {
+        const int c = lane % CH;
+        lds_blk = wave * NI;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int blk = wave * NI + i;     // 1 KiB block of the tile (wave-uniform)
-        const int row = blk * RPI + lane / CH;
-        const int s = min(k0 + row, T - 1);
-        const uint16_t *ks = kb + (size_t)s * row_stride + ((c ^ swz_k<D>(row)) << 3);
-        const uint16_t *vs = vb + (size_t)s * row_stride + ((c ^ swz_v<D>(row)) << 3);
-        __builtin_amdgcn_global_load_lds((const void *)ks, (lds_void *)(k_dst + blk * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void *)vs, (lds_void *)(v_dst + blk * 1024), 16, 0, 0);
+        for (int i = 0; i < NI; ++i) {
+            row[i] = (lds_blk + i) * RPI + lane / CH;
+            chunk_k[i] = (uint32_t)((c ^ swz_k<D>(row[i])) << 4);
+            chunk_v[i] = (uint32_t)((c ^ swz_v<D>(row[i])) << 4);
+            off_k[i] = (uint32_t)(row[i] * row_stride * 2) + chunk_k[i];
+            off_v[i] = (uint32_t)(row[i] * row_stride * 2) + chunk_v[i];
+        }
     }
-}
+
+    // rows k0 .. k0+63 of K and V (bases of the KV head) into dst_k / dst_v;
+    // rows past the sequence end are clamped to T - 1 (always masked)
+    __device__ __forceinline__ void issue(char *dst_k, char *dst_v, const uint16_t *__restrict__ kb,
+                                          const uint16_t *__restrict__ vb, size_t row_stride,
+                                          int k0, int T) const
+    {
+        const char *kt = (const char *)(kb + (size_t)k0 * row_stride);
+        const char *vt = (const char *)(vb + (size_t)k0 * row_stride);
+        if (k0 + kBN <= T) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                __builtin_amdgcn_global_load_lds((const void *)(kt + off_k[i]),
+                                                 (lds_void *)(dst_k + (lds_blk + i) * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void *)(vt + off_v[i]),
+                                                 (lds_void *)(dst_v + (lds_blk + i) * 1024), 16, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const uint32_t r = (uint32_t)min(row[i], T - 1 - k0) * (uint32_t)(row_stride * 2);
+                __builtin_amdgcn_global_load_lds((const void *)(kt + r + chunk_k[i]),
+                                                 (lds_void *)(dst_k + (lds_blk + i) * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void *)(vt + r + chunk_v[i]),
+                                                 (lds_void *)(dst_v + (lds_blk + i) * 1024), 16, 0, 0);
+            }
+        }
+    }
+};
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x16 &c)
 {
@@ -107,7 +142,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int half = lane >> 5;
     const int l32 = lane & 31;
 
@@ -151,7 +186,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const size_t row_stride = (size_t)hkv * D;
     const uint16_t *kb = k + ((size_t)start * hkv + kvh) * D;
     const uint16_t *vb = v + ((size_t)start * hkv + kvh) * D;
-    issue_tile<D>(lds, lds + TILE_BYTES, kb, vb, row_stride, 0, T, wave, lane);
+    TileLoader<D> loader;
+    loader.init(wave, lane, row_stride);
+    loader.issue(lds, lds + TILE_BYTES, kb, vb, row_stride, 0, T);
 
     // ---- Q^T operand in registers: lane holds row pw0 + l32, d = ks*16 + half*8 ..
     bf16x8 qreg[D / 16];
@@ -191,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
         if (it + 1 < n_tiles) {
             const int kn = (it + 1) < nA ? it + 1 : tB0 + (it + 1 - nA);
             char *nk = lds + ((it + 1) & 1) * 2 * TILE_BYTES;
-            issue_tile<D>(nk, nk + TILE_BYTES, kb, vb, row_stride, kn * kBN, T, wave, lane);
+            loader.issue(nk, nk + TILE_BYTES, kb, vb, row_stride, kn * kBN, T);
         }
         if (!wave_active || k0 > pw_last) continue;  // nothing visible for this wave
 
