@@ -245,39 +245,335 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     }
 }
 
-// o[b][h] = sum_s e^{lse_s - M} o_s / sum_s e^{lse_s - M}, ascending s.
+// ---------------------------------------------------------------------------
+// bf16 decode on the matrix cores.
+//
+// Per wavefront and 32-token chunk of its split:
+//   S^T = K Q^T   on v_mfma_f32_16x16x32_bf16: A = K (lane l: token l%16 of a
+//                 16-token half, 8 consecutive d), loaded straight from the
+//                 cache into registers (each instruction reads 64 contiguous
+//                 bytes of 16 rows); B = Q^T (lane l: head l%16, zero for
+//                 l%16 >= G), loaded once.  C lane l: head l%16, tokens
+//                 4*(l/16) + j of the half.
+//   softmax       per head over the lane's 8 tokens, lazy reference max.
+//   O^T += V^T P^T on the same MFMA: P^T is the lane's own C values (head l%16,
+//                 tokens 4*(l/16)+j of both halves -> k index 8*(l/16) + e);
+//                 V rows go global -> LDS (global_load_lds_dwordx4, swizzled)
+//                 and V^T comes back through ds_read_b64_tr_b16.
+// The chunk loop is software pipelined: the K registers and V LDS buffer of
+// chunk i+1 are requested before chunk i is computed.  The 4 wavefronts of the
+// workgroup take interleaved chunks and are merged with the log-sum-exp rule.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+
+constexpr int kDecChunk = 32;              // tokens per wavefront iteration
+constexpr float kDecRescaleSlack = 8.0f;   // log2 units
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// V tile swizzle: 16-byte chunk c of row r is stored at chunk c ^ (2 * (r % 8)),
+// so the 8 rows x 32 bytes a 32-lane transposed read touches hit disjoint banks.
+template <int D>
+__device__ __forceinline__ int dec_swz(int r) { return (2 * (r & 7)) & (D / 8 - 1); }
+
+template <int D>
+struct DecChunkRegs {
+    u32x4 k[2][D / 32];   // [half][d step] K operand
+};
+
+template <int D, int G, int MODE>
+__global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_new,
+    const uint16_t *__restrict__ v_new, uint16_t *__restrict__ k_cache,
+    uint16_t *__restrict__ v_cache, int max_cache, const int32_t *__restrict__ cache_len,
+    const uint8_t *__restrict__ route, int n_layers, int layer, int hq, int hkv, SparseRule rule,
+    float scale_log2, int split_tokens, int n_splits, float *__restrict__ o_part,
+    float *__restrict__ lse_part)
+{
+    constexpr int CH = D / 8;                 // 16-byte chunks per row
+    constexpr int RPI = 64 / CH;              // V rows per global_load_lds (1 KiB)
+    constexpr int VINS = kDecChunk / RPI;     // V copies per chunk per wave
+    constexpr int VBYTES = kDecChunk * D * 2; // one wave's V buffer
+    constexpr int NKS = D / 32;               // d steps of the QK product
+    static_assert(G >= 1 && G <= 16, "GQA ratio");
+    // V buffers: [wave] x 2, two separate arrays so that reads of the current
+    // chunk provably do not alias the copies into the next one
+    __shared__ __attribute__((aligned(1024))) char vbuf0[kWaves][VBYTES];
+    __shared__ __attribute__((aligned(1024))) char vbuf1[kWaves][VBYTES];
+    __shared__ float sm_m[kWaves][16];
+    __shared__ float sm_l[kWaves][16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15;   // head (C/B operands) or token (A operand)
+    const int g4 = lane >> 4;    // 16-lane group
+
+    const int split = blockIdx.x;
+    const int unit = blockIdx.y;
+    const int b = unit / hkv, kvh = unit % hkv;
+    const int n = cache_len[b];
+    if (n < 1 || n > max_cache) return;  // the merge kernel writes NaN for this sequence
+
+    const bool is_fa = MODE == kModeFA ? true
+                       : MODE == kModeSA ? false
+                                         : route[(size_t)b * n_layers + layer] != 0;
+    int sink_len, win_start;
+    if (is_fa) {
+        sink_len = n;
+        win_start = n;
+    } else {
+        const int i_q = (n - 1) >> rule.bk_log2;
+        sink_len = min(rule.ns << rule.bk_log2, n);
+        win_start = max(rule.ns << rule.bk_log2, (i_q - rule.nw + 1) << rule.bk_log2);
+        win_start = min(win_start, n);
+    }
+    const int kept = sink_len + (n - win_start);
+    const int v0 = split * split_tokens;
+    const int v1 = min(v0 + split_tokens, kept);
+
+    const size_t cache_base = ((size_t)b * hkv + kvh) * (size_t)max_cache * D;
+    const uint16_t *kc = k_cache + cache_base;
+    const uint16_t *vc = v_cache + cache_base;
+    const uint16_t *kn = k_new ? k_new + ((size_t)b * hkv + kvh) * D : nullptr;
+    const uint16_t *vn = v_new ? v_new + ((size_t)b * hkv + kvh) * D : nullptr;
+    // the workgroup whose split holds the new token appends it to the cache;
+    // every read of that position below goes to k_new / v_new instead
+    if (kn && v0 <= kept - 1 && kept - 1 < v1 && tid < CH) {
+        *(u32x4 *)(k_cache + cache_base + (size_t)(n - 1) * D + tid * 8) = *(const u32x4 *)(kn + tid * 8);
+        *(u32x4 *)(v_cache + cache_base + (size_t)(n - 1) * D + tid * 8) = *(const u32x4 *)(vn + tid * 8);
+    }
+
+    // physical row address of kept-token index v (clamped into the split)
+    auto row_ptr = [&](const uint16_t *cache, const uint16_t *fresh, int vi) -> const uint16_t * {
+        const int vv = min(vi, v1 - 1);
+        const int pos = vv < sink_len ? vv : win_start + (vv - sink_len);
+        return (fresh && pos == n - 1) ? fresh : cache + (size_t)pos * D;
+    };
+    auto issue = [&](int cv, DecChunkRegs<D> &r, char *vdst) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const uint16_t *kp = row_ptr(kc, kn, cv + hh * 16 + l16) + g4 * 8;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) r.k[hh][ks] = *(const u32x4 *)(kp + ks * 32);
+        }
+#pragma unroll
+        for (int i = 0; i < VINS; ++i) {
+            const int row = i * RPI + lane / CH;
+            const int c = lane % CH;
+            const uint16_t *vp = row_ptr(vc, vn, cv + row) + ((c ^ dec_swz<D>(row)) << 3);
+            __builtin_amdgcn_global_load_lds((const void *)vp, (lds_void_t *)(vdst + i * 1024), 16, 0, 0);
+        }
+    };
+
+    // Q^T operand: lane l holds head l%16 (zero past G), d = ks*32 + 8*(l/16) .. +8
+    bf16x8 qreg[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        u32x4 w = {0, 0, 0, 0};
+        if (l16 < G) w = *(const u32x4 *)(q + ((size_t)b * hq + kvh * G + l16) * D + ks * 32 + g4 * 8);
+        qreg[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+
+    f32x4 oacc[D / 16];
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{0, 0, 0, 0};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    // transposed V read: lane (group g4, a = l16/4, bq = l16%4) points at row
+    // K0 + a, d columns C0 + 4*bq, and receives rows K0..K0+3 at d = C0 + l16
+    const int tr_a = l16 >> 2;
+    const int tr_b = l16 & 3;
+
+    auto compute = [&](int cv, const DecChunkRegs<D> &r, const char *vsrc) {
+        f32x4 st[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            st[hh] = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                st[hh] = mfma16(__builtin_bit_cast(bf16x8, r.k[hh][ks]), qreg[ks], st[hh]);
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool ok = cv + hh * 16 + 4 * g4 + j < v1;
+                st[hh][j] = ok ? st[hh][j] * scale_log2 : -INFINITY;
+                mx = fmaxf(mx, st[hh][j]);
+            }
+        mx = fmaxf(mx, xor16(mx));
+        mx = max_xor32(mx);
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kDecRescaleSlack) != 0) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.0f : m_new));
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < D / 16; ++i) oacc[i] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+        float p[2][4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                p[hh][j] = fast_exp2(st[hh][j] - m_use);
+                l_run += p[hh][j];
+            }
+        const u32x4 pw = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                          pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+        const int r0 = 4 * g4 + tr_a;   // rows of half 0; half 1 is r0 + 16
+        const int r1 = r0 + 16;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            const int col = dt * 16 + 4 * tr_b;
+            const int off0 = r0 * (D * 2) + (((col >> 3) ^ dec_swz<D>(r0)) << 4) + (col & 7) * 2;
+            const int off1 = r1 * (D * 2) + (((col >> 3) ^ dec_swz<D>(r1)) << 4) + (col & 7) * 2;
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t *)(vsrc + off0));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t *)(vsrc + off1));
+            const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+            const u32x4 aw = {lo2[0], lo2[1], hi2[0], hi2[1]};
+            oacc[dt] = mfma16(__builtin_bit_cast(bf16x8, aw), pb, oacc[dt]);
+        }
+    };
+
+    // software-pipelined chunk loop, unrolled by two so each step uses fixed buffers
+    DecChunkRegs<D> ra, rb;
+    const int stride = kWaves * kDecChunk;
+    int cv = v0 + wave * kDecChunk;
+    if (cv < v1) issue(cv, ra, vbuf0[wave]);
+    while (cv < v1) {
+        const int cn = cv + stride;
+        if (cn < v1) issue(cn, rb, vbuf1[wave]);
+        if (cn < v1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NKS + VINS) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        compute(cv, ra, vbuf0[wave]);
+        if (cn >= v1) break;
+        const int cm = cn + stride;
+        if (cm < v1) issue(cm, ra, vbuf0[wave]);
+        if (cm < v1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NKS + VINS) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        compute(cn, rb, vbuf1[wave]);
+        cv = cm;
+    }
+
+    // per-head totals of this wavefront: lanes l16 + 16*g4 share head l16
+    float l_w = l_run + xor16(l_run);
+    l_w = sum_xor32(l_w);
+    // O^T: lane holds the finished sums for d = dt*16 + 4*g4 + j of head l16
+    __syncthreads();  // every wave is done with its V buffers: reuse them for the merge
+    float *sm_o = (float *)&vbuf0[0][0];   // [wave][16][D] floats (32 KiB at D = 128)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            sm_o[((size_t)wave * 16 + l16) * D + dt * 16 + 4 * g4 + j] = oacc[dt][j];
+    if (g4 == 0) {
+        sm_m[wave][l16] = m_run;
+        sm_l[wave][l16] = l_w;
+    }
+    __syncthreads();
+
+    // merge the 4 wavefronts in order; write this split's partial (o, lse)
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+        const int h = idx / D, d = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+        const float Mu = M == -INFINITY ? 0.0f : M;
+        float L = 0.0f, O = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = fast_exp2(sm_m[w][h] - Mu);
+            L += sm_l[w][h] * f;
+            O += sm_o[((size_t)w * 16 + h) * D + d] * f;
+        }
+        const size_t row = ((size_t)b * hq + kvh * G + h) * n_splits + split;
+        o_part[row * D + d] = L > 0.0f ? O / L : 0.0f;
+        if (d == 0) lse_part[row] = L > 0.0f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+    }
+}
+
+// o[b][h] = sum_s e^{lse_s - M} o_s / sum_s e^{lse_s - M}, M = max_s lse_s.
+// One workgroup per (sequence, query head); the max and the weight sum are
+// block reductions in a fixed tree, the weighted sum runs in ascending s per
+// output element, so the result does not depend on timing.
+constexpr int kMergeThreads = 128;
+constexpr int kMergeChunk = 1024;
+
+__device__ __forceinline__ float block_reduce(float v, float *red, bool is_max)
+{
+    const int tid = threadIdx.x;
+    red[tid] = v;
+    __syncthreads();
+    for (int off = kMergeThreads / 2; off > 0; off >>= 1) {
+        if (tid < off) red[tid] = is_max ? fmaxf(red[tid], red[tid + off]) : red[tid] + red[tid + off];
+        __syncthreads();
+    }
+    const float r = red[0];
+    __syncthreads();
+    return r;
+}
+
 template <typename TE>
-__global__ __launch_bounds__(64) void decode_merge_kernel(
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     const float *__restrict__ o_part, const float *__restrict__ lse_part,
     const int32_t *__restrict__ cache_len, int max_cache, int hq, int D, int n_splits,
     TE *__restrict__ o, float *__restrict__ lse)
 {
+    __shared__ float red[kMergeThreads];
+    __shared__ float wts[kMergeChunk];
     const int bh = blockIdx.x;
-    const int b = bh / hq;
-    const int n = cache_len[b];
+    const int tid = threadIdx.x;
+    const int n = cache_len[bh / hq];
     const bool bad = n < 1 || n > max_cache;
     const float *lp = lse_part + (size_t)bh * n_splits;
-    float M = -INFINITY;
-    if (!bad)
-        for (int s = 0; s < n_splits; ++s) M = fmaxf(M, lp[s]);
-    float W = 0.0f;
-    if (!bad)
-        for (int s = 0; s < n_splits; ++s) W += lp[s] == -INFINITY ? 0.0f : __expf(lp[s] - M);
-    const float inv = 1.0f / W;
-    for (int d = threadIdx.x; d < D; d += 64) {
-        float acc = 0.0f;
-        if (!bad)
-            for (int s = 0; s < n_splits; ++s) {
-                if (lp[s] == -INFINITY) continue;
-                acc += __expf(lp[s] - M) * o_part[((size_t)bh * n_splits + s) * D + d];
+
+    float m = -INFINITY;
+    for (int s = tid; s < n_splits; s += kMergeThreads) m = fmaxf(m, lp[s]);
+    const float M = block_reduce(m, red, true);
+    float w = 0.0f;
+    for (int s = tid; s < n_splits; s += kMergeThreads)
+        w += lp[s] == -INFINITY ? 0.0f : __expf(lp[s] - M);
+    const float W = block_reduce(w, red, false);
+
+    float acc = 0.0f;
+    const float *op = o_part + (size_t)bh * n_splits * D + tid;
+    for (int s0 = 0; s0 < n_splits; s0 += kMergeChunk) {
+        const int cnt = min(kMergeChunk, n_splits - s0);
+        for (int s = tid; s < cnt; s += kMergeThreads)
+            wts[s] = lp[s0 + s] == -INFINITY ? 0.0f : __expf(lp[s0 + s] - M);
+        __syncthreads();
+        if (tid < D) {
+            int s = 0;
+            for (; s + 8 <= cnt; s += 8) {
+                float x[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) x[u] = op[(size_t)(s0 + s + u) * D];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) acc += wts[s + u] * x[u];
             }
-        const float val = bad ? __builtin_nanf("") : acc * inv;
-        if constexpr (sizeof(TE) == 2)
-            ((uint16_t *)o)[(size_t)bh * D + d] = to_bf16(val);
-        else
-            ((float *)o)[(size_t)bh * D + d] = val;
+            for (; s < cnt; ++s) acc += wts[s] * op[(size_t)(s0 + s) * D];
+        }
+        __syncthreads();
     }
-    if (lse && threadIdx.x == 0) lse[bh] = bad ? __builtin_nanf("") : M + __logf(W);
+    if (tid < D) {
+        const float val = bad ? __builtin_nanf("") : acc / W;
+        if constexpr (sizeof(TE) == 2)
+            ((uint16_t *)o)[(size_t)bh * D + tid] = to_bf16(val);
+        else
+            ((float *)o)[(size_t)bh * D + tid] = val;
+    }
+    if (lse && tid == 0) lse[bh] = bad ? __builtin_nanf("") : M + __logf(W);
 }
 
 template <typename TE, int D, int G>
@@ -297,6 +593,40 @@ hipError_t launch_split(const DecodeArgs &a, hipStream_t stream, const SparseRul
         decode_split_kernel<TE, D, G, kModeMixed><<<grid, kThreads, 0, stream>>>(FA_DECODE_ARGS);
 #undef FA_DECODE_ARGS
     return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_bf16(const DecodeArgs &a, hipStream_t stream, const SparseRule &r,
+                       float scale_log2)
+{
+    dim3 grid(a.n_splits, a.batch * a.hkv);
+#define FA_DEC16_ARGS                                                                          \
+    (const uint16_t *)a.q, (const uint16_t *)a.k_new, (const uint16_t *)a.v_new,                 \
+        (uint16_t *)a.k_cache, (uint16_t *)a.v_cache, a.max_cache, a.cache_len, a.route,          \
+        a.n_layers, a.layer, a.hq, a.hkv, r, scale_log2, a.split_tokens, a.n_splits, a.o_part,    \
+        a.lse_part
+    if (a.mode == kModeFA)
+        decode_bf16_kernel<D, G, kModeFA><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
+    else if (a.mode == kModeSA)
+        decode_bf16_kernel<D, G, kModeSA><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
+    else
+        decode_bf16_kernel<D, G, kModeMixed><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
+#undef FA_DEC16_ARGS
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bf16_by_g(const DecodeArgs &a, hipStream_t stream, const SparseRule &r,
+                            float scale_log2)
+{
+    switch (a.hq / a.hkv) {
+    case 1: return launch_bf16<D, 1>(a, stream, r, scale_log2);
+    case 2: return launch_bf16<D, 2>(a, stream, r, scale_log2);
+    case 4: return launch_bf16<D, 4>(a, stream, r, scale_log2);
+    case 8: return launch_bf16<D, 8>(a, stream, r, scale_log2);
+    case 16: return launch_bf16<D, 16>(a, stream, r, scale_log2);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <typename TE, int D>
@@ -323,18 +653,18 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
     const float scale_log2 = a.sm_scale * kLog2e;
     hipError_t e;
     if (a.bf16)
-        e = a.d == 128 ? launch_by_g<uint16_t, 128>(a, stream, r, scale_log2)
-                       : launch_by_g<uint16_t, 64>(a, stream, r, scale_log2);
+        e = a.d == 128 ? launch_bf16_by_g<128>(a, stream, r, scale_log2)
+                       : launch_bf16_by_g<64>(a, stream, r, scale_log2);
     else
         e = a.d == 128 ? launch_by_g<float, 128>(a, stream, r, scale_log2)
                        : launch_by_g<float, 64>(a, stream, r, scale_log2);
     if (e != hipSuccess) return e;
     if (a.bf16)
-        decode_merge_kernel<uint16_t><<<a.batch * a.hq, 64, 0, stream>>>(
+        decode_merge_kernel<uint16_t><<<a.batch * a.hq, kMergeThreads, 0, stream>>>(
             a.o_part, a.lse_part, a.cache_len, a.max_cache, a.hq, a.d, a.n_splits, (uint16_t *)a.o,
             a.lse);
     else
-        decode_merge_kernel<float><<<a.batch * a.hq, 64, 0, stream>>>(
+        decode_merge_kernel<float><<<a.batch * a.hq, kMergeThreads, 0, stream>>>(
             a.o_part, a.lse_part, a.cache_len, a.max_cache, a.hq, a.d, a.n_splits, (float *)a.o,
             a.lse);
     return hipGetLastError();
