@@ -45,6 +45,7 @@ def parse():
     p.add_argument("--decode-len", type=int, default=131072, help="KV cache length in decode")
     p.add_argument("--decode-batch", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-sweep", action="store_true", help="skip the 8k/32k/64k prefill sweep")
     p.add_argument("--cpu-rows", type=int, default=192,
                    help="query rows of the FA layer the oracle times (SA gets 4x)")
     p.add_argument("--profile", action="store_true",
@@ -274,6 +275,45 @@ def main():
     torch.cuda.synchronize()
     t_decode_allfa = a.elapsed_time(b) * 1e-3
 
+    log("all-FA references done")
+
+    # ---- context sweep of the routed prefill (router + 32 layers), one pass each
+    sweep = []
+    if not args.no_sweep:
+        for Ts in (8192, 32768, 65536):
+            if Ts >= T:
+                continue
+            cu_s = torch.tensor([0, Ts], dtype=torch.int32, device=dev)
+            res = {}
+            for kind in ("routed", "all_fa"):
+                ms_pass = None
+                for rep in range(2):  # first pass warms up, second is timed
+                    a, b_ = ev(), ev()
+                    a.record(stream)
+                    _lib.fa_router_decide(x_q[:Ts], cu_s, POOL, w1, b1, w2, b2, route, logits,
+                                          ws_router)
+                    r_host = (route.cpu().numpy() if kind == "routed"
+                              else np.ones((1, N_LAYERS), np.uint8))
+                    r_dev = route if kind == "routed" else allfa
+                    for l in range(N_LAYERS):
+                        q, k, v = sets[l % n_sets]
+                        _lib.fa_attn_prefill(q[:Ts], k[:Ts], v[:Ts], o_pre[:Ts], cu_s, Ts, r_dev,
+                                             l, SINK, WINDOW, BLOCK, scale, route_host=r_host)
+                    b_.record(stream)
+                    torch.cuda.synchronize()
+                    ms_pass = a.elapsed_time(b_)
+                res[kind] = ms_pass
+                if kind == "routed":
+                    n_fa_s = int(route.cpu().numpy().sum())
+            sweep.append({"seq": Ts, "tok_s": round(Ts / res["routed"] * 1e3, 1),
+                          "ms": round(res["routed"], 3), "n_fa_layers": n_fa_s,
+                          "all_fa_ms": round(res["all_fa"], 3),
+                          "speedup_vs_all_fa": round(res["all_fa"] / res["routed"], 3)})
+        sweep.append({"seq": T, "tok_s": round(T / t_prefill, 1), "ms": round(t_prefill * 1e3, 3),
+                      "n_fa_layers": n_fa, "all_fa_ms": round(t_prefill_allfa * 1e3, 3),
+                      "speedup_vs_all_fa": round(t_prefill_allfa / t_prefill, 3)})
+        log("context sweep done")
+
     # ---- roofline --------------------------------------------------------------
     fa_flop = flops_of_pairs(pairs_fa(T))
     sa_flop = flops_of_pairs(pairs_sa(T))
@@ -317,6 +357,7 @@ def main():
             "sa_layer_tflops": round(sa_flop / t_sa / 1e12, 1) if sa_layers else None,
             "all_fa_ms": round(t_prefill_allfa * 1e3, 3),
             "speedup_vs_all_fa": round(t_prefill_allfa / t_prefill, 3),
+            "context_sweep": sweep,
         },
         "decode": {
             "tok_s": round(NB / t_decode, 1),
@@ -342,7 +383,6 @@ def main():
         },
     }
 
-    log("all-FA references done")
     # ---- CPU oracle baseline (rank 0, N=1 only) and sampled parity -------------
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity"] = cpu_baseline(
