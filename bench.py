@@ -177,6 +177,13 @@ def main():
             kc[b] = synth.device_normal((HKV, NC, D), seed=1000 + 64 * l + 2 * b)
             vc[b] = synth.device_normal((HKV, NC, D), seed=1001 + 64 * l + 2 * b)
         caches.append((kc, vc))
+    # compact SA ring caches (sink + window rows) for the SA layers of the decode stack
+    RING = SINK + WINDOW
+    rings = {}
+    for l in range(n_dec_layers):
+        if not dec_route_np[0, l]:
+            rings[l] = (synth.device_normal((NB, HKV, RING, D), seed=5000 + 2 * l),
+                        synth.device_normal((NB, HKV, RING, D), seed=5001 + 2 * l))
     q_dec = synth.device_normal((NB, HQ, D), seed=7)
     o_dec = torch.empty_like(q_dec)
     cache_len = torch.full((NB,), NC, dtype=torch.int32, device=dev)
@@ -277,6 +284,29 @@ def main():
 
     log("all-FA references done")
 
+    # ---- decode step with ring caches on the SA layers (persistent-KV saving)
+    ring_ms = []
+    for rep in range(args.warmup + args.steps):
+        a, b_ = ev(), ev()
+        a.record(stream)
+        for l in range(n_dec_layers):
+            if l in rings:
+                kr, vr = rings[l]
+                _lib.fa_attn_decode_ring(q_dec, o_dec, kr, vr, cache_len, SINK, WINDOW, BLOCK,
+                                         scale, workspace=ws_dec)
+            else:
+                kc, vc = caches[l]
+                _lib.fa_attn_decode(q_dec, o_dec, kc, vc, cache_len, dec_route, l, SINK, WINDOW,
+                                    BLOCK, scale, workspace=ws_dec, route_host=dec_route_np)
+        b_.record(stream)
+        torch.cuda.synchronize()
+        if rep >= args.warmup:
+            ring_ms.append(a.elapsed_time(b_))
+    t_decode_ring = float(np.mean(ring_ms)) * 1e-3
+    kv_full = 2 * n_dec_layers * NB * HKV * NC * D * 2
+    kv_ring = sum(2 * NB * HKV * (RING if l in rings else NC) * D * 2 for l in range(n_dec_layers))
+    log("ring-cache decode done")
+
     # ---- context sweep of the routed prefill (router + 32 layers), one pass each
     sweep = []
     if not args.no_sweep:
@@ -367,6 +397,11 @@ def main():
             "sa_layer_gbs": round(dec_sa_bytes / td_sa / 1e9, 1),
             "all_fa_ms": round(t_decode_allfa * 1e3, 4),
             "speedup_vs_all_fa": round(t_decode_allfa / t_decode, 3),
+            "ring_cache_tok_s": round(NB / t_decode_ring, 1),
+            "ring_cache_ms_per_token_step": round(t_decode_ring * 1e3, 4),
+            "persistent_kv_gib_full": round(kv_full / 2**30, 3),
+            "persistent_kv_gib_ring": round(kv_ring / 2**30, 3),
+            "persistent_kv_saving": round(1 - kv_ring / kv_full, 4),
         },
         "roofline": {
             "kernel": "prefill_bf16_kernel<128> (FA layer, 131072 tokens)",

@@ -224,6 +224,63 @@ fa_status fa_attn_decode(const void *q, void *o, float *lse, const void *k_new,
                          float sm_scale, void *workspace, size_t ws_bytes,
                          void *stream);
 
+/* ------------------------------------------------------------------------ */
+/* Compact KV cache for SA layers                                           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * An SA layer's decode only ever reads the sink tokens and the local window of
+ * blocks, so its persistent KV can shrink to sink + window tokens per (sequence,
+ * KV head): the "persistent KV saving" of SA layers reported by
+ * [thelatestinai paper page, Tables 15 and 16].  The ring layout of
+ * [batch][n_kv_heads][ring_tokens][head_dim], ring_tokens = sink + window:
+ *   position p < sink                -> row p;
+ *   position p in window block j     -> row sink + ((j - ns) mod nw) * block
+ *                                       + p mod block  (j = p / block >= ns),
+ * so a token that starts a new block takes the rows of the block that has just
+ * left the window.  The attention result is identical to the full cache.
+ */
+
+/*
+ * fa_kv_compact -- build the ring caches of one SA layer from its prefill K/V.
+ * For every sequence b (length T_b) it copies the tokens the next decode query
+ * (position T_b) keeps: positions [0, min(sink, T_b)) and the window blocks
+ * max(ns, T_b/block - nw + 1) .. T_b/block below T_b.  Other ring rows are left
+ * untouched (they are never read before being written).
+ * k, v [total][n_kv_heads][head_dim] (dtype), cu_seqlens [batch+1] int32 device;
+ * k_ring, v_ring [batch][n_kv_heads][ring_tokens][head_dim] (dtype) out.
+ * Errors: NULL pointer, batch/heads <= 0, bad sparse config, ring_tokens !=
+ * sink + window -> FA_ERR_INVALID_ARG; head_dim/dtype -> FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_kv_compact(const void *k, const void *v, int32_t dtype,
+                        const int32_t *cu_seqlens, int32_t batch,
+                        int32_t n_kv_heads, int32_t head_dim,
+                        int32_t sink_tokens, int32_t window_tokens,
+                        int32_t block_tokens, void *k_ring, void *v_ring,
+                        int32_t ring_tokens, void *stream);
+
+/*
+ * fa_attn_decode_ring -- fa_attn_decode for an SA layer whose caches are ring
+ * caches (every sequence is SA; no route argument).  cache_len[b] is the
+ * sequence length n including the new token (it may exceed ring_tokens); the
+ * query sits at position n - 1 and reads the sink and window tokens of query
+ * block (n - 1) / block from their ring rows.  k_new / v_new (nullable, both or
+ * neither) are appended at the ring row of position n - 1.  The workspace is
+ * fa_decode_workspace_size(batch, n_q_heads, head_dim, ring_tokens) bytes.
+ * Device behaviour: cache_len < 1 gives NaN outputs and touches no cache row.
+ * Errors: as fa_attn_decode, plus ring_tokens != sink + window ->
+ * FA_ERR_INVALID_ARG.
+ */
+fa_status fa_attn_decode_ring(const void *q, void *o, float *lse,
+                              const void *k_new, const void *v_new,
+                              void *k_ring, void *v_ring, int32_t ring_tokens,
+                              const int32_t *cache_len, int32_t dtype,
+                              int32_t batch, int32_t n_q_heads,
+                              int32_t n_kv_heads, int32_t head_dim,
+                              int32_t sink_tokens, int32_t window_tokens,
+                              int32_t block_tokens, float sm_scale,
+                              void *workspace, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

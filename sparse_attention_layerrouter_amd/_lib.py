@@ -22,6 +22,7 @@ FA_F32, FA_BF16 = 0, 1
 EXPORTS = (
     "fa_last_error", "fa_abi_version", "fa_router_workspace_size", "fa_router_decide",
     "fa_block_plan", "fa_attn_prefill", "fa_decode_workspace_size", "fa_attn_decode",
+    "fa_kv_compact", "fa_attn_decode_ring",
 )
 
 
@@ -62,6 +63,11 @@ def lib() -> ctypes.CDLL:
     L.fa_attn_decode.restype = I32
     L.fa_attn_decode.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, P, P, I32,
                                  I32, I32, I32, I32, F, P, SZ, P]
+    L.fa_kv_compact.restype = I32
+    L.fa_kv_compact.argtypes = [P, P, I32, P, I32, I32, I32, I32, I32, I32, P, P, I32, P]
+    L.fa_attn_decode_ring.restype = I32
+    L.fa_attn_decode_ring.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32,
+                                      I32, I32, F, P, SZ, P]
     _lib = L
     return _lib
 
@@ -193,3 +199,33 @@ def fa_attn_decode(q, o, k_cache, v_cache, cache_len, route, layer, sink_tokens,
         route.shape[1], layer, sink_tokens, window_tokens, block_tokens, float(sm_scale),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     del keep
+
+
+def fa_kv_compact(k, v, cu_seqlens, sink_tokens, window_tokens, block_tokens, k_ring, v_ring,
+                  stream=None):
+    """Build the SA ring caches [B, Hkv, sink + window, d] from prefill K/V [total, Hkv, d]."""
+    _require_cuda(k, v, cu_seqlens, k_ring, v_ring)
+    batch = cu_seqlens.numel() - 1
+    _, hkv, d = k.shape
+    _check(lib().fa_kv_compact(
+        _ptr(k), _ptr(v), _dtype_code(k), _ptr(cu_seqlens), batch, hkv, d, sink_tokens,
+        window_tokens, block_tokens, _ptr(k_ring), _ptr(v_ring), k_ring.shape[2],
+        _stream(stream)))
+
+
+def fa_attn_decode_ring(q, o, k_ring, v_ring, cache_len, sink_tokens, window_tokens,
+                        block_tokens, sm_scale, workspace=None, k_new=None, v_new=None, lse=None,
+                        stream=None):
+    """Decode step of an SA layer over ring caches [B, Hkv, sink + window, d]."""
+    import torch
+    _require_cuda(q, o, k_ring, v_ring, cache_len, k_new, v_new, lse)
+    batch, hq, d = q.shape
+    hkv, ring = k_ring.shape[1], k_ring.shape[2]
+    if workspace is None:
+        n = fa_decode_workspace_size(batch, hq, d, ring)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().fa_attn_decode_ring(
+        _ptr(q), _ptr(o), _ptr(lse), _ptr(k_new), _ptr(v_new), _ptr(k_ring), _ptr(v_ring), ring,
+        _ptr(cache_len), _dtype_code(q), batch, hq, hkv, d, sink_tokens, window_tokens,
+        block_tokens, float(sm_scale), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -85,7 +85,7 @@ extern "C" {
 
 const char *fa_last_error(void) { return g_last_error.c_str(); }
 
-int32_t fa_abi_version(void) { return 2; }
+int32_t fa_abi_version(void) { return 3; }
 
 size_t fa_router_workspace_size(int32_t batch, int32_t hidden, int32_t router_hidden)
 {
@@ -220,47 +220,53 @@ size_t fa_decode_workspace_size(int32_t batch, int32_t n_q_heads, int32_t head_d
     return round256(rows * head_dim * sizeof(float)) + round256(rows * sizeof(float));
 }
 
-fa_status fa_attn_decode(const void *q, void *o, float *lse, const void *k_new, const void *v_new,
-                         void *k_cache, void *v_cache, int32_t max_cache,
-                         const int32_t *cache_len, int32_t dtype, int32_t batch,
-                         int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
-                         const uint8_t *route, const uint8_t *route_host, int32_t n_layers,
-                         int32_t layer, int32_t sink_tokens, int32_t window_tokens,
-                         int32_t block_tokens, float sm_scale, void *workspace, size_t ws_bytes,
-                         void *stream)
+}  // extern "C"
+
+namespace {
+
+fa_status decode_impl(const char *fn, bool ring, const void *q, void *o, float *lse,
+                      const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                      int32_t max_cache, const int32_t *cache_len, int32_t dtype, int32_t batch,
+                      int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                      const uint8_t *route, const uint8_t *route_host, int32_t n_layers,
+                      int32_t layer, int32_t sink_tokens, int32_t window_tokens,
+                      int32_t block_tokens, float sm_scale, void *workspace, size_t ws_bytes,
+                      void *stream)
 {
-    if (!q || !o || !k_cache || !v_cache || !cache_len || !route)
-        return fail(FA_ERR_INVALID_ARG, "fa_attn_decode: a required pointer is NULL");
+    if (!q || !o || !k_cache || !v_cache || !cache_len || (!ring && !route))
+        return fail(FA_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
     if ((k_new == nullptr) != (v_new == nullptr))
-        return fail(FA_ERR_INVALID_ARG, "fa_attn_decode: give both k_new and v_new, or neither");
+        return fail(FA_ERR_INVALID_ARG, "%s: give both k_new and v_new, or neither", fn);
     if (batch <= 0 || max_cache <= 0)
-        return fail(FA_ERR_INVALID_ARG, "fa_attn_decode: batch=%d max_cache=%d must be positive",
-                    batch, max_cache);
+        return fail(FA_ERR_INVALID_ARG, "%s: batch=%d cache rows=%d must be positive", fn, batch,
+                    max_cache);
     if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0)
         return fail(FA_ERR_INVALID_ARG,
-                    "fa_attn_decode: n_q_heads=%d must be a positive multiple of n_kv_heads=%d",
+                    "%s: n_q_heads=%d must be a positive multiple of n_kv_heads=%d", fn,
                     n_q_heads, n_kv_heads);
-    if (n_layers <= 0 || layer < 0 || layer >= n_layers)
-        return fail(FA_ERR_INVALID_ARG, "fa_attn_decode: layer %d outside [0, %d)", layer,
-                    n_layers);
+    if (!ring && (n_layers <= 0 || layer < 0 || layer >= n_layers))
+        return fail(FA_ERR_INVALID_ARG, "%s: layer %d outside [0, %d)", fn, layer, n_layers);
     if (!std::isfinite(sm_scale) || sm_scale <= 0.0f)
-        return fail(FA_ERR_INVALID_ARG, "fa_attn_decode: sm_scale must be finite and > 0");
+        return fail(FA_ERR_INVALID_ARG, "%s: sm_scale must be finite and > 0", fn);
     fa::DecodeArgs a{};
     if (!sparse_cfg(sink_tokens, window_tokens, block_tokens, a.ns, a.nw, a.bk_log2))
-        return fail(FA_ERR_INVALID_ARG,
-                    "fa_attn_decode: bad sparse config sink=%d window=%d block=%d", sink_tokens,
-                    window_tokens, block_tokens);
+        return fail(FA_ERR_INVALID_ARG, "%s: bad sparse config sink=%d window=%d block=%d", fn,
+                    sink_tokens, window_tokens, block_tokens);
+    if (ring && max_cache != sink_tokens + window_tokens)
+        return fail(FA_ERR_INVALID_ARG, "%s: ring_tokens=%d must equal sink + window = %d", fn,
+                    max_cache, sink_tokens + window_tokens);
     if (dtype != FA_F32 && dtype != FA_BF16)
-        return fail(FA_ERR_UNSUPPORTED, "fa_attn_decode: dtype %d is not FA_F32/FA_BF16", dtype);
+        return fail(FA_ERR_UNSUPPORTED, "%s: dtype %d is not FA_F32/FA_BF16", fn, dtype);
     if (head_dim != 64 && head_dim != 128)
-        return fail(FA_ERR_UNSUPPORTED, "fa_attn_decode: head_dim %d not in {64, 128}", head_dim);
+        return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", fn, head_dim);
     const int G = n_q_heads / n_kv_heads;
     if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
-        return fail(FA_ERR_UNSUPPORTED, "fa_attn_decode: GQA ratio %d not in {1,2,4,8,16}", G);
+        return fail(FA_ERR_UNSUPPORTED, "%s: GQA ratio %d not in {1,2,4,8,16}", fn, G);
 
     // Grid sizing: kept tokens per sequence are at most max_cache, or at most
-    // sink + window when the host mirror says every sequence is SA here.
-    a.mode = route_mode(route_host, batch, n_layers, layer);
+    // sink + window for an SA layer.
+    a.ring = ring ? 1 : 0;
+    a.mode = ring ? fa::kModeSA : route_mode(route_host, batch, n_layers, layer);
     int max_kept = max_cache;
     if (a.mode == fa::kModeSA && sink_tokens + window_tokens < max_kept)
         max_kept = sink_tokens + window_tokens;
@@ -270,7 +276,7 @@ fa_status fa_attn_decode(const void *q, void *o, float *lse, const void *k_new, 
     const size_t o_bytes = round256(rows * head_dim * sizeof(float));
     const size_t need = o_bytes + round256(rows * sizeof(float));
     if (!workspace || ws_bytes < need)
-        return fail(FA_ERR_WORKSPACE, "fa_attn_decode: workspace %zu bytes, need %zu",
+        return fail(FA_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn,
                     workspace ? ws_bytes : (size_t)0, need);
     a.q = q;
     a.o = o;
@@ -287,12 +293,78 @@ fa_status fa_attn_decode(const void *q, void *o, float *lse, const void *k_new, 
     a.hkv = n_kv_heads;
     a.d = head_dim;
     a.route = route;
-    a.n_layers = n_layers;
-    a.layer = layer;
+    a.n_layers = ring ? 1 : n_layers;
+    a.layer = ring ? 0 : layer;
     a.sm_scale = sm_scale;
     a.o_part = (float *)workspace;
     a.lse_part = (float *)((char *)workspace + o_bytes);
-    return hip_status(fa::launch_decode(a, (hipStream_t)stream), "fa_attn_decode");
+    return hip_status(fa::launch_decode(a, (hipStream_t)stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_attn_decode(const void *q, void *o, float *lse, const void *k_new, const void *v_new,
+                         void *k_cache, void *v_cache, int32_t max_cache,
+                         const int32_t *cache_len, int32_t dtype, int32_t batch,
+                         int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                         const uint8_t *route, const uint8_t *route_host, int32_t n_layers,
+                         int32_t layer, int32_t sink_tokens, int32_t window_tokens,
+                         int32_t block_tokens, float sm_scale, void *workspace, size_t ws_bytes,
+                         void *stream)
+{
+    return decode_impl("fa_attn_decode", false, q, o, lse, k_new, v_new, k_cache, v_cache,
+                       max_cache, cache_len, dtype, batch, n_q_heads, n_kv_heads, head_dim, route,
+                       route_host, n_layers, layer, sink_tokens, window_tokens, block_tokens,
+                       sm_scale, workspace, ws_bytes, stream);
+}
+
+fa_status fa_attn_decode_ring(const void *q, void *o, float *lse, const void *k_new,
+                              const void *v_new, void *k_ring, void *v_ring, int32_t ring_tokens,
+                              const int32_t *cache_len, int32_t dtype, int32_t batch,
+                              int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                              int32_t sink_tokens, int32_t window_tokens, int32_t block_tokens,
+                              float sm_scale, void *workspace, size_t ws_bytes, void *stream)
+{
+    return decode_impl("fa_attn_decode_ring", true, q, o, lse, k_new, v_new, k_ring, v_ring,
+                       ring_tokens, cache_len, dtype, batch, n_q_heads, n_kv_heads, head_dim,
+                       nullptr, nullptr, 1, 0, sink_tokens, window_tokens, block_tokens, sm_scale,
+                       workspace, ws_bytes, stream);
+}
+
+fa_status fa_kv_compact(const void *k, const void *v, int32_t dtype, const int32_t *cu_seqlens,
+                        int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t sink_tokens,
+                        int32_t window_tokens, int32_t block_tokens, void *k_ring, void *v_ring,
+                        int32_t ring_tokens, void *stream)
+{
+    if (!k || !v || !cu_seqlens || !k_ring || !v_ring)
+        return fail(FA_ERR_INVALID_ARG, "fa_kv_compact: a required pointer is NULL");
+    if (batch <= 0 || n_kv_heads <= 0)
+        return fail(FA_ERR_INVALID_ARG, "fa_kv_compact: batch=%d n_kv_heads=%d must be positive",
+                    batch, n_kv_heads);
+    fa::CompactArgs a{};
+    if (!sparse_cfg(sink_tokens, window_tokens, block_tokens, a.ns, a.nw, a.bk_log2))
+        return fail(FA_ERR_INVALID_ARG, "fa_kv_compact: bad sparse config sink=%d window=%d block=%d",
+                    sink_tokens, window_tokens, block_tokens);
+    if (ring_tokens != sink_tokens + window_tokens)
+        return fail(FA_ERR_INVALID_ARG, "fa_kv_compact: ring_tokens=%d must equal sink + window = %d",
+                    ring_tokens, sink_tokens + window_tokens);
+    if (dtype != FA_F32 && dtype != FA_BF16)
+        return fail(FA_ERR_UNSUPPORTED, "fa_kv_compact: dtype %d is not FA_F32/FA_BF16", dtype);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(FA_ERR_UNSUPPORTED, "fa_kv_compact: head_dim %d not in {64, 128}", head_dim);
+    a.k = k;
+    a.v = v;
+    a.bf16 = dtype == FA_BF16;
+    a.cu_seqlens = cu_seqlens;
+    a.batch = batch;
+    a.hkv = n_kv_heads;
+    a.d = head_dim;
+    a.k_ring = k_ring;
+    a.v_ring = v_ring;
+    a.ring = ring_tokens;
+    return hip_status(fa::launch_kv_compact(a, (hipStream_t)stream), "fa_kv_compact");
 }
 
 }  // extern "C"

@@ -58,7 +58,27 @@ __device__ __forceinline__ int phys_of(int v, int sink_len, int win_start)
     return v < sink_len ? v : win_start + (v - sink_len);
 }
 
-template <typename TE, int D, int G, int MODE>
+// Row of position pos in a compact SA ring cache of sink + window tokens: the
+// sink tokens keep their positions; window block j (j >= ns) lives in ring
+// block (j - ns) mod nw, so the newest block overwrites the one that just left
+// the window.
+__device__ __forceinline__ int ring_slot(int pos, const SparseRule &r)
+{
+    const int sink_tok = r.ns << r.bk_log2;
+    if (pos < sink_tok) return pos;
+    const int j = pos >> r.bk_log2;
+    return sink_tok + (((j - r.ns) % r.nw) << r.bk_log2) + (pos & ((1 << r.bk_log2) - 1));
+}
+
+// Row of position pos in the cache: the position itself, or its ring slot.
+template <bool RING>
+__device__ __forceinline__ int cache_row(int pos, const SparseRule &r)
+{
+    if constexpr (RING) return ring_slot(pos, r);
+    else return pos;
+}
+
+template <typename TE, int D, int G, int MODE, bool RING>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const TE *__restrict__ q, const TE *__restrict__ k_new, const TE *__restrict__ v_new,
     TE *__restrict__ k_cache, TE *__restrict__ v_cache, int max_cache,
@@ -85,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const int unit = blockIdx.y;
     const int b = unit / hkv, kvh = unit % hkv;
     const int n = cache_len[b];
-    if (n < 1 || n > max_cache) return;  // merge kernel writes NaN for this sequence
+    if (n < 1 || (!RING && n > max_cache)) return;  // merge kernel writes NaN for this sequence
 
     const bool is_fa = MODE == kModeFA ? true
                        : MODE == kModeSA ? false
@@ -140,13 +160,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
             ok[u] = vi < v1;
             pos[u] = ok[u] ? phys_of(vi, sink_len, win_start) : 0;
             const bool fresh = ok[u] && kn && pos[u] == n - 1;
-            const TE *kp = fresh ? kn + c * EPL : kc + (size_t)pos[u] * D + c * EPL;
-            const TE *vp = fresh ? vn + c * EPL : vc + (size_t)pos[u] * D + c * EPL;
+            const size_t row = (size_t)cache_row<RING>(pos[u], rule);
+            const TE *kp = fresh ? kn + c * EPL : kc + row * D + c * EPL;
+            const TE *vp = fresh ? vn + c * EPL : vc + row * D + c * EPL;
             kw[u] = ok[u] ? *(const u32x4 *)kp : u32x4{0, 0, 0, 0};
             vw[u] = ok[u] ? *(const u32x4 *)vp : u32x4{0, 0, 0, 0};
             if (fresh) {  // append the new token to the cache
-                *(u32x4 *)(k_cache + cache_base + (size_t)pos[u] * D + c * EPL) = kw[u];
-                *(u32x4 *)(v_cache + cache_base + (size_t)pos[u] * D + c * EPL) = vw[u];
+                *(u32x4 *)(k_cache + cache_base + row * D + c * EPL) = kw[u];
+                *(u32x4 *)(v_cache + cache_base + row * D + c * EPL) = vw[u];
             }
         }
         // scores (log2 domain), reduced over the LPR lanes of each row
@@ -285,7 +306,7 @@ struct DecChunkRegs {
     u32x4 k[2][D / 32];   // [half][d step] K operand
 };
 
-template <int D, int G, int MODE>
+template <int D, int G, int MODE, bool RING>
 __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_new,
     const uint16_t *__restrict__ v_new, uint16_t *__restrict__ k_cache,
@@ -317,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
     const int unit = blockIdx.y;
     const int b = unit / hkv, kvh = unit % hkv;
     const int n = cache_len[b];
-    if (n < 1 || n > max_cache) return;  // the merge kernel writes NaN for this sequence
+    if (n < 1 || (!RING && n > max_cache)) return;  // the merge kernel writes NaN for it
 
     const bool is_fa = MODE == kModeFA ? true
                        : MODE == kModeSA ? false
@@ -344,15 +365,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
     // the workgroup whose split holds the new token appends it to the cache;
     // every read of that position below goes to k_new / v_new instead
     if (kn && v0 <= kept - 1 && kept - 1 < v1 && tid < CH) {
-        *(u32x4 *)(k_cache + cache_base + (size_t)(n - 1) * D + tid * 8) = *(const u32x4 *)(kn + tid * 8);
-        *(u32x4 *)(v_cache + cache_base + (size_t)(n - 1) * D + tid * 8) = *(const u32x4 *)(vn + tid * 8);
+        const size_t row = (size_t)cache_row<RING>(n - 1, rule);
+        *(u32x4 *)(k_cache + cache_base + row * D + tid * 8) = *(const u32x4 *)(kn + tid * 8);
+        *(u32x4 *)(v_cache + cache_base + row * D + tid * 8) = *(const u32x4 *)(vn + tid * 8);
     }
 
     // physical row address of kept-token index v (clamped into the split)
     auto row_ptr = [&](const uint16_t *cache, const uint16_t *fresh, int vi) -> const uint16_t * {
         const int vv = min(vi, v1 - 1);
         const int pos = vv < sink_len ? vv : win_start + (vv - sink_len);
-        return (fresh && pos == n - 1) ? fresh : cache + (size_t)pos * D;
+        return (fresh && pos == n - 1) ? fresh : cache + (size_t)cache_row<RING>(pos, rule) * D;
     };
     auto issue = [&](int cv, DecChunkRegs<D> &r, char *vdst) {
 #pragma unroll
@@ -535,7 +557,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     const int bh = blockIdx.x;
     const int tid = threadIdx.x;
     const int n = cache_len[bh / hq];
-    const bool bad = n < 1 || n > max_cache;
+    const bool bad = n < 1 || n > max_cache;  // max_cache: INT_MAX for ring caches
     const float *lp = lse_part + (size_t)bh * n_splits;
 
     float m = -INFINITY;
@@ -585,12 +607,14 @@ hipError_t launch_split(const DecodeArgs &a, hipStream_t stream, const SparseRul
     (const TE *)a.q, (const TE *)a.k_new, (const TE *)a.v_new, (TE *)a.k_cache,                 \
         (TE *)a.v_cache, a.max_cache, a.cache_len, a.route, a.n_layers, a.layer, a.hq, a.hkv, r, \
         scale_log2, a.split_tokens, a.n_splits, a.o_part, a.lse_part
-    if (a.mode == kModeFA)
-        decode_split_kernel<TE, D, G, kModeFA><<<grid, kThreads, 0, stream>>>(FA_DECODE_ARGS);
+    if (a.ring)
+        decode_split_kernel<TE, D, G, kModeSA, true><<<grid, kThreads, 0, stream>>>(FA_DECODE_ARGS);
+    else if (a.mode == kModeFA)
+        decode_split_kernel<TE, D, G, kModeFA, false><<<grid, kThreads, 0, stream>>>(FA_DECODE_ARGS);
     else if (a.mode == kModeSA)
-        decode_split_kernel<TE, D, G, kModeSA><<<grid, kThreads, 0, stream>>>(FA_DECODE_ARGS);
+        decode_split_kernel<TE, D, G, kModeSA, false><<<grid, kThreads, 0, stream>>>(FA_DECODE_ARGS);
     else
-        decode_split_kernel<TE, D, G, kModeMixed><<<grid, kThreads, 0, stream>>>(FA_DECODE_ARGS);
+        decode_split_kernel<TE, D, G, kModeMixed, false><<<grid, kThreads, 0, stream>>>(FA_DECODE_ARGS);
 #undef FA_DECODE_ARGS
     return hipGetLastError();
 }
@@ -605,12 +629,14 @@ hipError_t launch_bf16(const DecodeArgs &a, hipStream_t stream, const SparseRule
         (uint16_t *)a.k_cache, (uint16_t *)a.v_cache, a.max_cache, a.cache_len, a.route,          \
         a.n_layers, a.layer, a.hq, a.hkv, r, scale_log2, a.split_tokens, a.n_splits, a.o_part,    \
         a.lse_part
-    if (a.mode == kModeFA)
-        decode_bf16_kernel<D, G, kModeFA><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
+    if (a.ring)
+        decode_bf16_kernel<D, G, kModeSA, true><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
+    else if (a.mode == kModeFA)
+        decode_bf16_kernel<D, G, kModeFA, false><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
     else if (a.mode == kModeSA)
-        decode_bf16_kernel<D, G, kModeSA><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
+        decode_bf16_kernel<D, G, kModeSA, false><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
     else
-        decode_bf16_kernel<D, G, kModeMixed><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
+        decode_bf16_kernel<D, G, kModeMixed, false><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
 #undef FA_DEC16_ARGS
     return hipGetLastError();
 }
@@ -659,15 +685,71 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
         e = a.d == 128 ? launch_by_g<float, 128>(a, stream, r, scale_log2)
                        : launch_by_g<float, 64>(a, stream, r, scale_log2);
     if (e != hipSuccess) return e;
+    const int max_len = a.ring ? 0x7fffffff : a.max_cache;
     if (a.bf16)
         decode_merge_kernel<uint16_t><<<a.batch * a.hq, kMergeThreads, 0, stream>>>(
-            a.o_part, a.lse_part, a.cache_len, a.max_cache, a.hq, a.d, a.n_splits, (uint16_t *)a.o,
+            a.o_part, a.lse_part, a.cache_len, max_len, a.hq, a.d, a.n_splits, (uint16_t *)a.o,
             a.lse);
     else
         decode_merge_kernel<float><<<a.batch * a.hq, kMergeThreads, 0, stream>>>(
-            a.o_part, a.lse_part, a.cache_len, a.max_cache, a.hq, a.d, a.n_splits, (float *)a.o,
+            a.o_part, a.lse_part, a.cache_len, max_len, a.hq, a.d, a.n_splits, (float *)a.o,
             a.lse);
     return hipGetLastError();
+}
+
+namespace {
+
+// Copy the tokens an SA layer keeps for the next decode query of every sequence
+// (position T_b, query block i = T_b / block) from the packed prefill K/V into
+// the compact ring cache: positions [0, min(sink, T_b)) and the window blocks
+// max(ns, i - nw + 1) .. i below T_b.  One thread moves 16 bytes.
+template <typename TE, int D>
+__global__ __launch_bounds__(256) void kv_compact_kernel(
+    const TE *__restrict__ k, const TE *__restrict__ v, const int32_t *__restrict__ cu, int hkv,
+    SparseRule rule, TE *__restrict__ k_ring, TE *__restrict__ v_ring, int ring)
+{
+    constexpr int EPL = 16 / sizeof(TE);
+    constexpr int LPR = D / EPL;            // threads per row
+    constexpr int ROWS = 256 / LPR;         // rows per workgroup
+    const int unit = blockIdx.y;
+    const int b = unit / hkv, kvh = unit % hkv;
+    const int start = cu[b];
+    const int T = cu[b + 1] - start;
+    const int vi = blockIdx.x * ROWS + threadIdx.x / LPR;  // kept-token index
+    const int c = threadIdx.x % LPR;
+    if (T <= 0) return;
+    const int i_q = T >> rule.bk_log2;
+    const int sink_tok = rule.ns << rule.bk_log2;
+    const int sink_len = min(sink_tok, T);
+    const int win_start = min(max(sink_tok, (i_q - rule.nw + 1) << rule.bk_log2), T);
+    const int kept = sink_len + (T - win_start);
+    if (vi >= kept) return;
+    const int pos = vi < sink_len ? vi : win_start + (vi - sink_len);
+    const size_t src = ((size_t)(start + pos) * hkv + kvh) * D + c * EPL;
+    const size_t dst = (((size_t)b * hkv + kvh) * ring + ring_slot(pos, rule)) * D + c * EPL;
+    *(u32x4 *)(k_ring + dst) = *(const u32x4 *)(k + src);
+    *(u32x4 *)(v_ring + dst) = *(const u32x4 *)(v + src);
+}
+
+template <typename TE, int D>
+hipError_t launch_compact_t(const CompactArgs &a, hipStream_t stream)
+{
+    constexpr int ROWS = 256 / (D / (16 / sizeof(TE)));
+    SparseRule r{a.ns, a.nw, a.bk_log2};
+    dim3 grid((a.ring + ROWS - 1) / ROWS, a.batch * a.hkv);
+    kv_compact_kernel<TE, D><<<grid, 256, 0, stream>>>((const TE *)a.k, (const TE *)a.v,
+                                                        a.cu_seqlens, a.hkv, r, (TE *)a.k_ring,
+                                                        (TE *)a.v_ring, a.ring);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_kv_compact(const CompactArgs &a, hipStream_t stream)
+{
+    if (a.bf16) return a.d == 128 ? launch_compact_t<uint16_t, 128>(a, stream)
+                                  : launch_compact_t<uint16_t, 64>(a, stream);
+    return a.d == 128 ? launch_compact_t<float, 128>(a, stream) : launch_compact_t<float, 64>(a, stream);
 }
 
 }  // namespace fa

@@ -72,12 +72,24 @@ struct DecodeArgs {
     int ns, nw, bk_log2;
     float sm_scale;
     int mode;          // kModeMixed / kModeFA / kModeSA
+    int ring;          // caches are compact SA rings of max_cache = sink + window rows
     int split_tokens;  // KV tokens per split (multiple of 64)
     int n_splits;      // splits launched per (sequence, kv head)
     float *o_part;     // [batch][hq][n_splits][d]
     float *lse_part;   // [batch][hq][n_splits]
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+struct CompactArgs {
+    const void *k, *v;
+    int bf16;
+    const int32_t *cu_seqlens;
+    int batch, hkv, d;
+    int ns, nw, bk_log2;
+    void *k_ring, *v_ring;
+    int ring;  // rows per (sequence, kv head) = sink + window
+};
+hipError_t launch_kv_compact(const CompactArgs &a, hipStream_t stream);
 
 // Split policy shared by fa_decode_workspace_size and fa_attn_decode.
 int decode_split_tokens(int max_kept_tokens);

@@ -27,14 +27,14 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 10, names
     assert set(names) == set(_lib.EXPORTS)
     for name in names:
         assert hasattr(L, name), name
 
 
 def test_abi_version_and_clean_error_state():
-    assert _lib.fa_abi_version() == 2
+    assert _lib.fa_abi_version() == 3
 
 
 def test_workspace_sizes():
@@ -157,3 +157,41 @@ def test_block_plan_validation(kw):
                            "block", "plan", "stream")]
     assert _lib.lib().fa_block_plan(*args) == _lib.FA_ERR_INVALID_ARG
     assert _lib.last_error().startswith("fa_block_plan")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kr=None), _lib.FA_ERR_INVALID_ARG),
+    (dict(ring=2000), _lib.FA_ERR_INVALID_ARG),      # not sink + window
+    (dict(block=24), _lib.FA_ERR_INVALID_ARG),
+    (dict(batch=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(d=32), _lib.FA_ERR_UNSUPPORTED),
+    (dict(dtype=2), _lib.FA_ERR_UNSUPPORTED),
+])
+def test_kv_compact_validation(kw, status):
+    a = dict(k=P, v=P, dtype=1, cu=P, batch=2, hkv=8, d=128, sink=128, window=2048, block=64,
+             kr=P, vr=P, ring=2176, stream=None)
+    a.update(kw)
+    args = [a[k] for k in ("k", "v", "dtype", "cu", "batch", "hkv", "d", "sink", "window",
+                           "block", "kr", "vr", "ring", "stream")]
+    assert _lib.lib().fa_kv_compact(*args) == status
+    assert _lib.last_error().startswith("fa_kv_compact")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), _lib.FA_ERR_INVALID_ARG),
+    (dict(ring=4096), _lib.FA_ERR_INVALID_ARG),      # not sink + window
+    (dict(k_new=P), _lib.FA_ERR_INVALID_ARG),
+    (dict(hq=30), _lib.FA_ERR_INVALID_ARG),
+    (dict(d=48), _lib.FA_ERR_UNSUPPORTED),
+    (dict(ws_bytes=16), _lib.FA_ERR_WORKSPACE),
+])
+def test_decode_ring_validation(kw, status):
+    a = dict(q=P, o=P, lse=None, k_new=None, v_new=None, kr=P, vr=P, ring=2176, cl=P, dtype=1,
+             batch=2, hq=32, hkv=8, d=128, sink=128, window=2048, block=64, scale=0.088, ws=P,
+             ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    args = [a[k] for k in ("q", "o", "lse", "k_new", "v_new", "kr", "vr", "ring", "cl", "dtype",
+                           "batch", "hq", "hkv", "d", "sink", "window", "block", "scale", "ws",
+                           "ws_bytes", "stream")]
+    assert _lib.lib().fa_attn_decode_ring(*args) == status
+    assert _lib.last_error().startswith("fa_attn_decode_ring")
