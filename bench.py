@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--decode-batch", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-sweep", action="store_true", help="skip the 8k/32k/64k prefill sweep")
+    p.add_argument("--no-serving", action="store_true",
+                   help="skip the batched decode sweep (batch 8/16/24/32 at a 32K context)")
     p.add_argument("--cpu-rows", type=int, default=192,
                    help="query rows of the FA layer the oracle times (SA gets 4x)")
     p.add_argument("--profile", action="store_true",
@@ -307,6 +309,77 @@ def main():
     kv_ring = sum(2 * NB * HKV * (RING if l in rings else NC) * D * 2 for l in range(n_dec_layers))
     log("ring-cache decode done")
 
+    # ---- batched-serving decode sweep at a 32K context (batch 8/16/24/32): the
+    # caches of each batch are prefix views of the per-layer buffers above
+    serving = []
+    if not args.no_serving and not args.profile and NB * NC >= 32 * 32768:
+        SC = 32768
+        rings32 = {l: (torch.empty((32, HKV, RING, D), dtype=torch.bfloat16, device=dev),
+                       torch.empty((32, HKV, RING, D), dtype=torch.bfloat16, device=dev))
+                   for l in rings}
+        for l, (kr, vr) in rings32.items():
+            kr.copy_(synth.device_normal((32, HKV, RING, D), seed=7000 + l))
+            vr.copy_(synth.device_normal((32, HKV, RING, D), seed=7100 + l))
+        ws_s = torch.empty(_lib.fa_decode_workspace_size(32, HQ, D, SC), dtype=torch.uint8,
+                           device=dev)
+        for bs in (8, 16, 24, 32):
+            q_s = synth.device_normal((bs, HQ, D), seed=8000 + bs)
+            o_s = torch.empty_like(q_s)
+            cl_s = torch.full((bs,), SC, dtype=torch.int32, device=dev)
+            r_np = np.array([[1 if l % 2 == 0 else 0 for l in range(N_LAYERS)]] * bs, np.uint8)
+            r_d = torch.from_numpy(r_np).to(dev)
+            ms = {}
+            for kind in ("full", "ring"):
+                times = []
+                for rep in range(3):
+                    a, b_ = ev(), ev()
+                    a.record(stream)
+                    for l in range(n_dec_layers):
+                        kc, vc = caches[l]
+                        n_el = bs * HKV * SC * D
+                        kcv = kc.view(-1)[:n_el].view(bs, HKV, SC, D)
+                        vcv = vc.view(-1)[:n_el].view(bs, HKV, SC, D)
+                        if kind == "ring" and l in rings32:
+                            kr, vr = rings32[l]
+                            _lib.fa_attn_decode_ring(q_s, o_s, kr[:bs], vr[:bs], cl_s, SINK, WINDOW,
+                                                     BLOCK, scale, workspace=ws_s)
+                        else:
+                            _lib.fa_attn_decode(q_s, o_s, kcv, vcv, cl_s, r_d, l, SINK, WINDOW,
+                                                BLOCK, scale, workspace=ws_s, route_host=r_np)
+                    b_.record(stream)
+                    torch.cuda.synchronize()
+                    if rep:
+                        times.append(a.elapsed_time(b_))
+                ms[kind] = float(np.mean(times))
+            # the all-FA reference on the same caches
+            r_fa = torch.ones((bs, N_LAYERS), dtype=torch.uint8, device=dev)
+            times = []
+            for rep in range(3):
+                a, b_ = ev(), ev()
+                a.record(stream)
+                for l in range(n_dec_layers):
+                    kc, vc = caches[l]
+                    n_el = bs * HKV * SC * D
+                    _lib.fa_attn_decode(q_s, o_s, kc.view(-1)[:n_el].view(bs, HKV, SC, D),
+                                        vc.view(-1)[:n_el].view(bs, HKV, SC, D), cl_s, r_fa, l,
+                                        SINK, WINDOW, BLOCK, scale, workspace=ws_s)
+                b_.record(stream)
+                torch.cuda.synchronize()
+                if rep:
+                    times.append(a.elapsed_time(b_))
+            ms_fa = float(np.mean(times))
+            kv_full_s = 2 * n_dec_layers * bs * HKV * SC * D * 2
+            kv_ring_s = sum(2 * bs * HKV * (RING if l in rings32 else SC) * D * 2
+                            for l in range(n_dec_layers))
+            serving.append({"batch": bs, "tok_s": round(bs / ms["full"] * 1e3, 1),
+                            "ring_cache_tok_s": round(bs / ms["ring"] * 1e3, 1),
+                            "all_fa_tok_s": round(bs / ms_fa * 1e3, 1),
+                            "speedup_vs_all_fa": round(ms_fa / ms["full"], 3),
+                            "persistent_kv_gib_full": round(kv_full_s / 2**30, 3),
+                            "persistent_kv_gib_ring": round(kv_ring_s / 2**30, 3)})
+        del rings32
+        log("serving sweep done")
+
     # ---- context sweep of the routed prefill (router + 32 layers), one pass each
     sweep = []
     if not args.no_sweep:
@@ -402,6 +475,7 @@ def main():
             "persistent_kv_gib_full": round(kv_full / 2**30, 3),
             "persistent_kv_gib_ring": round(kv_ring / 2**30, 3),
             "persistent_kv_saving": round(1 - kv_ring / kv_full, 4),
+            "serving_sweep_32k": serving,
         },
         "roofline": {
             "kernel": "prefill_bf16_kernel<128> (FA layer, 131072 tokens)",
