@@ -13,10 +13,12 @@
 //   S^T = K Q^T  on v_mfma_f32_32x32x16_bf16 (K from LDS, Q^T in registers);
 //   online softmax in the exp2 domain, row statistics per lane;
 //   O^T += V^T P^T on the same MFMA; P^T comes straight out of the S^T
-//   accumulators (no cross-lane movement) and V^T is staged transposed in LDS.
-// K is stored row-major with a 16-byte XOR swizzle, V^T with an 8-byte XOR
-// swizzle; both make the MFMA operand reads and the tile writes bank-conflict
-// free.  Global->register prefetch of tile i+1 overlaps the MFMAs of tile i.
+//   accumulators (no cross-lane movement) and V^T is read from the row-major
+//   V tile by the transposing LDS read ds_read_b64_tr_b16.
+// K and V tiles go global -> LDS directly (global_load_lds_dwordx4) into a
+// double buffer, each with a 16-byte XOR swizzle chosen so the MFMA operand
+// reads are bank-conflict free; the copy of tile i+1 is in flight while tile i
+// is computed.
 // The causal diagonal and the lower window edge are masked per element, all
 // other kept tiles run unmasked.
 //
