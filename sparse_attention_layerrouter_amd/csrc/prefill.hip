@@ -25,6 +25,8 @@
 // Generic kernel (fp32, and bf16 shapes the MFMA kernel does not cover): one
 // thread per (query row, head), exact online softmax over the same kept
 // ranges.  It is the correctness path for fp32 inputs.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -68,8 +70,11 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 // Asynchronous global -> LDS copies of one 64-key K tile and V tile.  Wave
 // instruction i of wave w fills 1 KiB block (w * NI + i) of a tile: lane l lands
 // at row (block * RPI + l / CH), chunk l % CH, and fetches the logical chunk the
-// swizzle stores there.  The per-lane byte offsets inside a full tile are fixed,
-// so they are computed once; only the tile base moves (a scalar).
+// swizzle stores there.  The copies are buffer loads: the tile base lives in a
+// scalar buffer descriptor and each lane's byte offset inside a full tile is a
+// fixed 32-bit register, so moving to the next tile costs no vector work.
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
 template <int D>
 struct TileLoader {
     static constexpr int CH = D / 8;              // 16-byte chunks per row
@@ -100,24 +105,26 @@ struct TileLoader {
                                           const uint16_t *__restrict__ vb, size_t row_stride,
                                           int k0, int T) const
     {
-        const char *kt = (const char *)(kb + (size_t)k0 * row_stride);
-        const char *vt = (const char *)(vb + (size_t)k0 * row_stride);
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(kb + (size_t)k0 * row_stride), (short)0, 0x7fffffff, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(vb + (size_t)k0 * row_stride), (short)0, 0x7fffffff, kRsrcWord3);
         if (k0 + kBN <= T) {
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                __builtin_amdgcn_global_load_lds((const void *)(kt + off_k[i]),
-                                                 (lds_void *)(dst_k + (lds_blk + i) * 1024), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void *)(vt + off_v[i]),
-                                                 (lds_void *)(dst_v + (lds_blk + i) * 1024), 16, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rk, (lds_void *)(dst_k + (lds_blk + i) * 1024), 16, (int)off_k[i], 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rv, (lds_void *)(dst_v + (lds_blk + i) * 1024), 16, (int)off_v[i], 0, 0, 0);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const uint32_t r = (uint32_t)min(row[i], T - 1 - k0) * (uint32_t)(row_stride * 2);
-                __builtin_amdgcn_global_load_lds((const void *)(kt + r + chunk_k[i]),
-                                                 (lds_void *)(dst_k + (lds_blk + i) * 1024), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void *)(vt + r + chunk_v[i]),
-                                                 (lds_void *)(dst_v + (lds_blk + i) * 1024), 16, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rk, (lds_void *)(dst_k + (lds_blk + i) * 1024), 16, (int)(r + chunk_k[i]), 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rv, (lds_void *)(dst_v + (lds_blk + i) * 1024), 16, (int)(r + chunk_v[i]), 0, 0, 0);
             }
         }
     }
@@ -208,11 +215,31 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const int my_t = min(pw0 + l32, T - 1);  // query position of this lane's row
     const int my_win_lo = ((my_t >> rule.bk_log2) - rule.nw + 1) << rule.bk_log2;
 
-    // transposed V reads: lane (group g, a = (l%16)/4, bq = l%4) points at key row
-    // K0 + a, d columns C0 + 4 bq .. +3; the instruction hands lane l the 4 keys
-    // K0 .. K0+3 at d = C0 + l%16.
-    const int tr_a = (lane & 15) >> 2;
-    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // Per-lane LDS byte offsets, fixed for the whole kernel (the buffer and the
+    // 32-key block only add constants, which become instruction offsets):
+    //   K operand of d step ks: key l32 (+32 for the second block), logical
+    //   chunk 2 ks + half, stored at chunk ^ swz_k(key) -- swz_k(key) depends on
+    //   l32 only.
+    //   V^T operand of d block dt: the transposed read of lane (a = (l%16)/4,
+    //   bq = l%4) points at key row 4 half + a (+16 per k step, +8 for the upper
+    //   4 keys), d columns C0 + 4 bq .. +3 with C0 = 32 dt + 16 ((l/16) % 2); the
+    //   instruction hands lane l the 4 keys of its group at d = C0 + l%16.  The
+    //   V swizzle depends on key row % 4 = a only.
+    uint32_t koff[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+        koff[ks] = (uint32_t)tile_off<D>(l32, ks * 2 + half, swz_k<D>(l32));
+    uint32_t voff[D / 32];
+    {
+        const int tr_a = (lane & 15) >> 2;
+        const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const int r0 = 4 * half + tr_a;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            const int col = dt * 32 + tr_col;
+            voff[dt] = (uint32_t)(tile_off<D>(r0, col >> 3, swz_v<D>(r0)) + (col & 7) * 2);
+        }
+    }
 
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -220,19 +247,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     float m_run = -INFINITY;  // reference max, log2 domain
     float l_run = 0.0f;       // this lane's share of the row sum
 
-    for (int it = 0; it < n_tiles; ++it) {
+    // One KV tile; BUF (the LDS buffer it sits in) is a compile-time constant so
+    // every LDS address is a fixed register plus an instruction offset.
+    auto tile_step = [&](auto buf_tag, int it) {
+        constexpr int BUF = decltype(buf_tag)::value;
         const int kt = it < nA ? it : tB0 + (it - nA);
         const int k0 = kt * kBN;
-        const char *k_lds = lds + (it & 1) * 2 * TILE_BYTES;
-        const char *v_lds = k_lds + TILE_BYTES;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();  // tile `it` landed; the other buffer is free again
         if (it + 1 < n_tiles) {
             const int kn = (it + 1) < nA ? it + 1 : tB0 + (it + 1 - nA);
-            char *nk = lds + ((it + 1) & 1) * 2 * TILE_BYTES;
+            char *nk = lds + (1 - BUF) * 2 * TILE_BYTES;
             loader.issue(nk, nk + TILE_BYTES, kb, vb, row_stride, kn * kBN, T);
         }
-        if (!wave_active || k0 > pw_last) continue;  // nothing visible for this wave
+        if (!wave_active || k0 > pw_last) return;  // nothing visible for this wave
+        constexpr uint32_t kbase = BUF * 2 * TILE_BYTES;
+        constexpr uint32_t vbase = kbase + TILE_BYTES;
 
         // ---- S^T = K Q^T : two 32-key blocks
         f32x16 s[2];
@@ -242,9 +272,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
         for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2) {
-                const int key = kb2 * 32 + l32;
-                bf16x8 a = __builtin_bit_cast(
-                    bf16x8, *(const u32x4 *)(k_lds + tile_off<D>(key, ks * 2 + half, swz_k<D>(key))));
+                const uint32_t off = koff[ks] + kbase + kb2 * 32 * D * 2;
+                bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4 *)(lds + off));
                 s[kb2] = mfma32(a, qreg[ks], s[kb2]);
             }
         }
@@ -305,20 +334,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
             const int kb2 = ksv >> 1, jb = (ksv & 1) * 4;
             u32x4 pw = {pk[kb2][jb], pk[kb2][jb + 1], pk[kb2][jb + 2], pk[kb2][jb + 3]};
             bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-            const int r0 = 16 * ksv + 4 * half + tr_a;  // key row of this lane's pointer
-            const int r1 = r0 + 8;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
-                const int col = dt * 32 + tr_col;   // d column of this lane's pointer
-                const int off_lo = tile_off<D>(r0, col >> 3, swz_v<D>(r0)) + (col & 7) * 2;
-                const int off_hi = tile_off<D>(r1, col >> 3, swz_v<D>(r1)) + (col & 7) * 2;
-                i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(v_lds + off_lo));
-                i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(v_lds + off_hi));
+                const uint32_t off_lo = voff[dt] + vbase + ksv * 16 * D * 2;
+                const uint32_t off_hi = off_lo + 8 * D * 2;
+                i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(lds + off_lo));
+                i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(lds + off_hi));
                 u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
                 u32x4 aw = {lo2[0], lo2[1], hi2[0], hi2[1]};
                 oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, aw), pb, oacc[dt]);
             }
         }
+    };
+
+    for (int it = 0; it < n_tiles; it += 2) {
+        tile_step(std::integral_constant<int, 0>{}, it);
+        if (it + 1 < n_tiles) tile_step(std::integral_constant<int, 1>{}, it + 1);
     }
 
     if (!wave_active) return;
