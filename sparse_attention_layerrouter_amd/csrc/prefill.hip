@@ -33,8 +33,9 @@
 namespace fa {
 namespace {
 
-constexpr int kBN = 64;        // keys per KV tile
-constexpr int kThreads = 256;  // 4 wavefronts
+constexpr int kBN = 64;                // keys per KV tile
+constexpr int kWaves = 8;              // two ping-pong groups of 4 wavefronts
+constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 // ---------------------------------------------------------------------------
@@ -67,23 +68,25 @@ __device__ __forceinline__ int tile_off(int row, int chunk, int swz)
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 
-// Asynchronous global -> LDS copies of one 64-key K tile and V tile.  Wave
-// instruction i of wave w fills 1 KiB block (w * NI + i) of a tile: lane l lands
-// at row (block * RPI + l / CH), chunk l % CH, and fetches the logical chunk the
-// swizzle stores there.  The copies are buffer loads: the tile base lives in a
-// scalar buffer descriptor and each lane's byte offset inside a full tile is a
-// fixed 32-bit register, so moving to the next tile costs no vector work.
+// Asynchronous global -> LDS copies of one 64-key K or V tile by the 4 waves of
+// ping-pong group 0.  Wave instruction i of wave w fills 1 KiB block (w * NI + i)
+// of the tile: lane l lands at row (block * RPI + l / CH), chunk l % CH, and
+// fetches the logical chunk the swizzle stores there.  The copies are buffer
+// loads: the tile base lives in a scalar buffer descriptor and each lane's byte
+// offset inside a full tile is a fixed 32-bit register, so a copy costs no
+// vector work.  The descriptor's size ends at the sequence end: rows past it
+// read as zero (and are masked).
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kLoadWaves = 4;
 
-template <int D>
+template <int D, bool IS_V>
 struct TileLoader {
-    static constexpr int CH = D / 8;              // 16-byte chunks per row
-    static constexpr int RPI = 64 / CH;           // rows per wave instruction (1 KiB)
-    static constexpr int NI = kBN / (RPI * 4);    // instructions per wave per tensor
-    uint32_t off_k[NI], off_v[NI];                // byte offsets inside a full tile
-    int row[NI];                                  // tile row of each instruction
-    int lds_blk;                                  // first 1 KiB block of this wave
-    uint32_t chunk_k[NI], chunk_v[NI];
+    static constexpr int CH = D / 8;                     // 16-byte chunks per row
+    static constexpr int RPI = 64 / CH;                  // rows per wave instruction (1 KiB)
+    static constexpr int NI = kBN / (RPI * kLoadWaves);  // instructions per wave
+    static_assert(NI >= 1 && NI * RPI * kLoadWaves == kBN, "tile split over the waves");
+    uint32_t off[NI];    // byte offset inside a full tile
+    int lds_blk;         // first 1 KiB block of this wave
 
     __device__ __forceinline__ void init(int wave, int lane, size_t row_stride)
     {
@@ -91,42 +94,25 @@ struct TileLoader {
         lds_blk = wave * NI;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            row[i] = (lds_blk + i) * RPI + lane / CH;
-            chunk_k[i] = (uint32_t)((c ^ swz_k<D>(row[i])) << 4);
-            chunk_v[i] = (uint32_t)((c ^ swz_v<D>(row[i])) << 4);
-            off_k[i] = (uint32_t)(row[i] * row_stride * 2) + chunk_k[i];
-            off_v[i] = (uint32_t)(row[i] * row_stride * 2) + chunk_v[i];
+            const int row = (lds_blk + i) * RPI + lane / CH;
+            const int chunk = c ^ (IS_V ? swz_v<D>(row) : swz_k<D>(row));
+            off[i] = (uint32_t)(row * row_stride * 2) + (uint32_t)(chunk << 4);
         }
     }
 
-    // rows k0 .. k0+63 of K and V (bases of the KV head) into dst_k / dst_v;
-    // rows past the sequence end are clamped to T - 1 (always masked)
-    __device__ __forceinline__ void issue(char *dst_k, char *dst_v, const uint16_t *__restrict__ kb,
-                                          const uint16_t *__restrict__ vb, size_t row_stride,
-                                          int k0, int T) const
+    // descriptor of rows k0 .. T-1 of one KV head
+    static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint16_t *__restrict__ base,
+                                                               size_t row_stride, int k0, int T)
     {
-        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(kb + (size_t)k0 * row_stride), (short)0, 0x7fffffff, kRsrcWord3);
-        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(vb + (size_t)k0 * row_stride), (short)0, 0x7fffffff, kRsrcWord3);
-        if (k0 + kBN <= T) {
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rk, (lds_void *)(dst_k + (lds_blk + i) * 1024), 16, (int)off_k[i], 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rv, (lds_void *)(dst_v + (lds_blk + i) * 1024), 16, (int)off_v[i], 0, 0, 0);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const uint32_t r = (uint32_t)min(row[i], T - 1 - k0) * (uint32_t)(row_stride * 2);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rk, (lds_void *)(dst_k + (lds_blk + i) * 1024), 16, (int)(r + chunk_k[i]), 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rv, (lds_void *)(dst_v + (lds_blk + i) * 1024), 16, (int)(r + chunk_v[i]), 0, 0, 0);
-            }
-        }
+        const long long bytes = (long long)(T - k0) * (long long)row_stride * 2;
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(base + (size_t)k0 * row_stride), (short)0,
+                                                 (int)min(bytes, 0x7fffffffLL), kRsrcWord3);
+    }
+
+    __device__ __forceinline__ void issue_one(int i, char *dst, __amdgpu_buffer_rsrc_t r) const
+    {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + (lds_blk + i) * 1024), 16,
+                                                 (int)off[i], 0, 0, 0);
     }
 };
 
@@ -135,10 +121,24 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// One workgroup: 4 waves x 32 query rows.  Wave w handles head
-// h0 + w / WPH and positions p0 + (w % WPH) * 32 .. +32, WPH = 4 / HPW.
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+// One workgroup: two groups of 4 waves, 32 query rows per wave.  In group g,
+// wave w handles head h0 + w / WPH and positions p0 + g * GP + (w % WPH) * 32
+// .. +32, WPH = 4 / HPW, GP = 32 * WPH.
+//
+// Ping-pong: a wave's work on KV tile t is an MFMA block M_t (O^T += V^T P^T
+// of tile t-1, then S^T = K Q^T of tile t) followed by a VALU block V_t (mask,
+// online softmax, P of tile t).  Group 0 runs M_0 V_0 M_1 V_1 ..., group 1 the
+// same one phase later, and every phase ends at a workgroup barrier, so while
+// one group's softmax occupies the vector ALUs the other group's products
+// occupy the matrix cores of the same SIMDs.  The barriers also order the
+// double-buffered tiles: at phase 2j every wave waits for the copies it issued
+// at phase 2j-2 (K of tile j, V of tile j-1) and issues K of tile j+1 and V of
+// tile j into the buffers whose previous tiles were last read at phase 2j-1.
 template <int D, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
     const int32_t *__restrict__ cu, const uint8_t *__restrict__ route, int n_layers, int layer,
@@ -146,12 +146,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     SparseRule rule, float scale_log2)
 {
     constexpr int TILE_BYTES = kBN * D * 2;
-    // [buffer][K, V] tiles, double-buffered
-    __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * TILE_BYTES];
+    // separate arrays per buffer: the compiler can then tell that reads of one
+    // buffer never wait for the asynchronous copies into the other
+    __shared__ __attribute__((aligned(1024))) char k_lds0[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char k_lds1[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char v_lds0[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char v_lds1[TILE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int grp = wave >> 2;
+    const int wq = wave & 3;
     const int half = lane >> 5;
     const int l32 = lane & 31;
 
@@ -169,17 +175,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 
     const int start = cu[b];
     const int T = cu[b + 1] - start;
-    const int wph = 4 / hpw;             // waves per head
-    const int bm_pos = 32 * wph;         // positions per workgroup
-    const int p0 = ptile * bm_pos;
-    if (p0 >= T) return;
-    const int p1 = min(p0 + bm_pos, T);
+    const int wph = 4 / hpw;        // waves per head in a group
+    const int gpos = 32 * wph;      // positions per group
+    const int p0 = ptile * 2 * gpos;
+    if (p0 >= T) return;            // uniform: the whole workgroup leaves
+    const int p1 = min(p0 + 2 * gpos, T);
     const bool is_fa = MODE == kModeFA ? true
                        : MODE == kModeSA ? false
                                          : route[(size_t)b * n_layers + layer] != 0;
 
-    const int h = kvh * G + hg * hpw + wave / wph;
-    const int pw0 = p0 + (wave % wph) * 32;   // this wave's first position
+    const int h = kvh * G + hg * hpw + wq / wph;
+    const int pw0 = p0 + grp * gpos + (wq % wph) * 32;  // this wave's first position
     const bool wave_active = pw0 < T;
     const int pw_last = min(pw0 + 31, T - 1);  // last valid position of the wave
 
@@ -191,13 +197,30 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const int tB1 = (p1 + kBN - 1) / kBN;
     const int nB = max(0, tB1 - tB0);
     const int n_tiles = nA + nB;
+    auto tile_k0 = [&](int t) __attribute__((always_inline)) { return (t < nA ? t : tB0 + (t - nA)) * kBN; };
 
     const size_t row_stride = (size_t)hkv * D;
     const uint16_t *kb = k + ((size_t)start * hkv + kvh) * D;
     const uint16_t *vb = v + ((size_t)start * hkv + kvh) * D;
-    TileLoader<D> loader;
-    loader.init(wave, lane, row_stride);
-    loader.issue(lds, lds + TILE_BYTES, kb, vb, row_stride, 0, T);
+    TileLoader<D, false> lk;
+    TileLoader<D, true> lv;
+    lk.init(wq, lane, row_stride);
+    lv.init(wq, lane, row_stride);
+    // Clear the tile buffers once: a copy past the sequence end may leave rows
+    // unwritten, and the first MFMA block multiplies a zero P with v_lds1; both
+    // then see zeros, never stale bit patterns.
+    for (int i = tid; i < TILE_BYTES / 16; i += kThreads) {
+        *(u32x4 *)(k_lds0 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+        *(u32x4 *)(k_lds1 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+        *(u32x4 *)(v_lds0 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+        *(u32x4 *)(v_lds1 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+    if (grp == 0) {
+        const __amdgpu_buffer_rsrc_t r0 = lk.rsrc(kb, row_stride, tile_k0(0), T);
+#pragma unroll
+        for (int i = 0; i < lk.NI; ++i) lk.issue_one(i, k_lds0, r0);
+    }
 
     // ---- Q^T operand in registers: lane holds row pw0 + l32, d = ks*16 + half*8 ..
     bf16x8 qreg[D / 16];
@@ -211,12 +234,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 
     // masking thresholds for this wave
     const int sink_tok = rule.ns << rule.bk_log2;
+    const int win_lo_min = ((pw0 >> rule.bk_log2) - rule.nw + 1) << rule.bk_log2;
     const int win_lo_max = ((pw_last >> rule.bk_log2) - rule.nw + 1) << rule.bk_log2;
     const int my_t = min(pw0 + l32, T - 1);  // query position of this lane's row
     const int my_win_lo = ((my_t >> rule.bk_log2) - rule.nw + 1) << rule.bk_log2;
+    // does any row of this wave see a key of the tile at k0?
+    auto wave_sees = [&](int k0) __attribute__((always_inline)) {
+        return wave_active && k0 <= pw_last &&
+               (is_fa || k0 < sink_tok || k0 + kBN > win_lo_min);
+    };
 
-    // Per-lane LDS byte offsets, fixed for the whole kernel (the buffer and the
-    // 32-key block only add constants, which become instruction offsets):
+    // Per-lane LDS byte offsets, fixed for the whole kernel (the 32-key block
+    // and the k step only add constants, which become instruction offsets):
     //   K operand of d step ks: key l32 (+32 for the second block), logical
     //   chunk 2 ks + half, stored at chunk ^ swz_k(key) -- swz_k(key) depends on
     //   l32 only.
@@ -246,39 +275,109 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
     float m_run = -INFINITY;  // reference max, log2 domain
     float l_run = 0.0f;       // this lane's share of the row sum
+    f32x16 s[2];              // S^T of the current tile (two 32-key blocks)
+    uint32_t pk[2][8];        // P of the previous tile, bf16 pairs (0: none)
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pk[kb2][j] = 0u;
+    bool s_live = false;      // s holds a tile this wave sees
 
-    // One KV tile; BUF (the LDS buffer it sits in) is a compile-time constant so
-    // every LDS address is a fixed register plus an instruction offset.
-    auto tile_step = [&](auto buf_tag, int it) {
-        constexpr int BUF = decltype(buf_tag)::value;
-        const int kt = it < nA ? it : tB0 + (it - nA);
-        const int k0 = kt * kBN;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();  // tile `it` landed; the other buffer is free again
-        if (it + 1 < n_tiles) {
-            const int kn = (it + 1) < nA ? it + 1 : tB0 + (it + 1 - nA);
-            char *nk = lds + (1 - BUF) * 2 * TILE_BYTES;
-            loader.issue(nk, nk + TILE_BYTES, kb, vb, row_stride, kn * kBN, T);
+    // ---- MFMA block of tile t: S^T = K Q^T of tile t, O^T += V^T P^T of tile t-1
+    // Operand reads from LDS: the K operand of d step ks / key block kb2, and
+    // the V^T operand of k step ksv / d block dt (two transposed reads).
+    // P^T for k-step ksv is the lane's own S^T values 8*(ksv%2) .. +8 of block
+    // ksv/2: k index 8*half + e <-> key 16*ksv + 8*(e/4) + 4*half + e%4.
+    auto k_operand = [&](const char *k_lds, int ks, int kb2) __attribute__((always_inline)) {
+        return __builtin_bit_cast(bf16x8, *(const u32x4 *)(k_lds + koff[ks] + kb2 * 32 * D * 2));
+    };
+    auto v_operand = [&](const char *v_lds, int ksv, int dt) __attribute__((always_inline)) {
+        const char *plo = v_lds + voff[dt] + ksv * 16 * D * 2;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)plo);
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(plo + 8 * D * 2));
+        u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        u32x4 aw = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        return __builtin_bit_cast(bf16x8, aw);
+    };
+    auto p_operand = [&](int ksv) __attribute__((always_inline)) {
+        const int kb2 = ksv >> 1, jb = (ksv & 1) * 4;
+        u32x4 pw = {pk[kb2][jb], pk[kb2][jb + 1], pk[kb2][jb + 2], pk[kb2][jb + 3]};
+        return __builtin_bit_cast(bf16x8, pw);
+    };
+    // Both products run as one pipeline: round r issues the two QK MFMAs of d
+    // step r and two PV MFMAs, so six accumulator chains are in flight, and
+    // every operand is read kLook MFMAs ahead; scheduling barriers pin the
+    // order.  The block has no branches: a tile this wave does not see still
+    // runs QK (the result is dropped) and its P is zero, so PV adds exactly 0.
+    //
+    // When LD is set (group 0 at even phases 2j) the block also issues the
+    // copies of K of tile j+1 and V of tile j, one every 4 MFMAs, so the memory
+    // pipeline drains while the matrix cores work and group 1's softmax is not
+    // interrupted.  Past the last tile the copies repeat the last tile into
+    // buffers nobody reads again.
+    auto block_mfma = [&](auto ld_tag, const char *k_lds, const char *v_lds, int t, char *kdst,
+                          char *vdst) __attribute__((always_inline)) {
+        constexpr bool LD = decltype(ld_tag)::value != 0;
+        constexpr int NR = D / 16;       // rounds
+        constexpr int NM = 4 * NR;       // MFMAs
+        constexpr int kLook = 6;
+        constexpr int NDT = D / 32;
+        constexpr int NLD = lk.NI + lv.NI;
+        static_assert(4 * NLD <= NM, "copies fit between the MFMAs");
+        s_live = t < n_tiles && wave_sees(tile_k0(t));
+        __amdgpu_buffer_rsrc_t rk, rv;
+        if constexpr (LD) {
+            rk = lk.rsrc(kb, row_stride, tile_k0(min(t + 1, n_tiles - 1)), T);
+            rv = lv.rsrc(vb, row_stride, tile_k0(min(t, n_tiles - 1)), T);
         }
-        if (!wave_active || k0 > pw_last) return;  // nothing visible for this wave
-        constexpr uint32_t kbase = BUF * 2 * TILE_BYTES;
-        constexpr uint32_t vbase = kbase + TILE_BYTES;
-
-        // ---- S^T = K Q^T : two 32-key blocks
-        f32x16 s[2];
         s[0] = f32x16{};
         s[1] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) {
-                const uint32_t off = koff[ks] + kbase + kb2 * 32 * D * 2;
-                bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4 *)(lds + off));
-                s[kb2] = mfma32(a, qreg[ks], s[kb2]);
+        bf16x8 ops[NM];
+        auto load_op = [&](int m) __attribute__((always_inline)) {
+            const int r = m >> 2, j = m & 3;
+            if (j < 2) {
+                ops[m] = k_operand(k_lds, r, j);
+            } else {
+                const int qv = 2 * r + (j - 2);
+                ops[m] = v_operand(v_lds, qv / NDT, qv % NDT);
             }
+        };
+#pragma unroll
+        for (int m = 0; m < kLook; ++m) load_op(m);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const int r = m >> 2, j = m & 3;
+            if (j < 2) {
+                s[j] = mfma32(ops[m], qreg[r], s[j]);
+            } else {
+                const int qv = 2 * r + (j - 2);
+                oacc[qv % NDT] = mfma32(ops[m], p_operand(qv / NDT), oacc[qv % NDT]);
+            }
+            if (m + kLook < NM) load_op(m + kLook);
+            if constexpr (LD) {
+                if ((m & 3) == 1 && (m >> 2) < NLD) {
+                    const int i = m >> 2;
+                    if (i < lk.NI) lk.issue_one(i, kdst, rk);
+                    else lv.issue_one(i - lk.NI, vdst, rv);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
+    };
 
-        // ---- mask (causal diagonal, window lower edge, sequence tail)
+    // ---- VALU block of tile t: mask, online softmax, P = bf16(2^(s - m))
+    auto block_valu = [&](int t) __attribute__((always_inline)) {
+        if (!s_live) {
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) pk[kb2][j] = 0u;
+            return;
+        }
+        const int k0 = tile_k0(t);
+        // mask (causal diagonal, window lower edge, sequence tail)
         const bool need_mask = (k0 + kBN - 1 > pw0) ||
                                (!is_fa && k0 < win_lo_max && k0 + kBN > sink_tok);
         if (need_mask) {
@@ -292,11 +391,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
                     if (!vis) s[kb2][j] = -INFINITY;
                 }
         }
-
-        // ---- online softmax (exp2 domain) with a lazily moved reference max:
-        // the reference m_ref only moves when a row's tile max exceeds it by more
-        // than kRescaleSlack (log2 units), so p = 2^(s - m_ref) <= 2^kRescaleSlack
-        // and the O / l rescale runs on few tiles.  O / l is independent of the
+        // online softmax (exp2 domain) with a lazily moved reference max: the
+        // reference only moves when a row's tile max exceeds it by more than
+        // kRescaleSlack (log2 units), so p = 2^(s - m_ref) <= 2^kRescaleSlack and
+        // the O / l rescale runs on few tiles.  O / l does not depend on the
         // reference, so the result is the same softmax.
         float mx = -INFINITY;
 #pragma unroll
@@ -314,7 +412,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
         }
         const float m_use = m_run == -INFINITY ? 0.0f : m_run;
         float psum = 0.0f;
-        uint32_t pk[2][8];
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -325,32 +422,46 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
                 pk[kb2][j / 2] = pack_bf16x2(e0, e1);
             }
         l_run += psum;
-
-        // ---- O^T += V^T P^T : 4 k-steps of 16 keys.  P^T for k-step ksv is the
-        // lane's own S^T values 8*(ksv%2) .. +8 of block ksv/2: k index
-        // 8*half + e <-> key 16*ksv + 8*(e/4) + 4*half + e%4.
-#pragma unroll
-        for (int ksv = 0; ksv < 4; ++ksv) {
-            const int kb2 = ksv >> 1, jb = (ksv & 1) * 4;
-            u32x4 pw = {pk[kb2][jb], pk[kb2][jb + 1], pk[kb2][jb + 2], pk[kb2][jb + 3]};
-            bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                const uint32_t off_lo = voff[dt] + vbase + ksv * 16 * D * 2;
-                const uint32_t off_hi = off_lo + 8 * D * 2;
-                i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(lds + off_lo));
-                i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(lds + off_hi));
-                u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-                u32x4 aw = {lo2[0], lo2[1], hi2[0], hi2[1]};
-                oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, aw), pb, oacc[dt]);
-            }
-        }
     };
 
-    for (int it = 0; it < n_tiles; it += 2) {
-        tile_step(std::integral_constant<int, 0>{}, it);
-        if (it + 1 < n_tiles) tile_step(std::integral_constant<int, 1>{}, it + 1);
-    }
+    // ---- phases.  Even phase 2j: wait for this wave's copies, barrier, then
+    // copy K of tile j+1 and V of tile j.  Odd phases: barrier only.
+    // Phase barriers are bare s_barrier instructions (a memory clobber keeps the
+    // compiler from moving LDS accesses across them): a workgroup fence would
+    // also wait for copies that have two phases to land.  At even phases every
+    // wave first waits for its own copies and LDS reads.
+    auto sync_even = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    const int n_phases = 2 * n_tiles + 2;
+    // Unrolled by 4 phases so every buffer choice is a compile-time constant;
+    // tile 2m's K sits in k_lds0, tile 2m+1's in k_lds1, V likewise.
+    auto run = [&](auto grp_tag) __attribute__((always_inline)) {
+        constexpr int GRP = decltype(grp_tag)::value;
+        for (int p = 0; p < n_phases; p += 4) {
+            const int t0 = p >> 1;  // even tile index of this round
+            sync_even();
+            if (GRP == 0) block_mfma(ic<1>{}, k_lds0, v_lds1, t0, k_lds1, v_lds0);
+            else if (p > 0) block_valu(t0 - 1);
+            if (p + 1 >= n_phases) break;
+            asm volatile("s_barrier" ::: "memory");
+            if (GRP == 0) block_valu(t0);
+            else block_mfma(ic<0>{}, k_lds0, v_lds1, t0, nullptr, nullptr);
+            if (p + 2 >= n_phases) break;
+            sync_even();
+            if (GRP == 0) block_mfma(ic<1>{}, k_lds1, v_lds0, t0 + 1, k_lds0, v_lds1);
+            else block_valu(t0);
+            if (p + 3 >= n_phases) break;
+            asm volatile("s_barrier" ::: "memory");
+            if (GRP == 0) block_valu(t0 + 1);
+            else block_mfma(ic<0>{}, k_lds1, v_lds0, t0 + 1, nullptr, nullptr);
+        }
+    };
+    if (grp == 0) run(ic<0>{});
+    else run(ic<1>{});
+    // the last even phase issued copies nobody reads: let them land before the
+    // workgroup (and its LDS) goes away
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     if (!wave_active) return;
     // ---- epilogue: O = O^T / l, lse = (m + log2 l) ln 2
@@ -466,7 +577,7 @@ hipError_t launch_mfma(const PrefillArgs &a, hipStream_t stream, const SparseRul
     const int G = a.hq / a.hkv;
     const int hpw = G >= 4 ? 4 : G;
     const int n_hgroups = G / hpw;
-    const int bm_pos = 32 * (4 / hpw);
+    const int bm_pos = 2 * 32 * (4 / hpw);  // two groups of 4 waves x 32 rows
     const int n_ptiles = (a.max_seqlen + bm_pos - 1) / bm_pos;
     const int n_units = a.batch * a.hkv;
     const long long n_wg = (long long)n_ptiles * n_hgroups * n_units;
