@@ -396,11 +396,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         // kRescaleSlack (log2 units), so p = 2^(s - m_ref) <= 2^kRescaleSlack and
         // the O / l rescale runs on few tiles.  O / l does not depend on the
         // reference, so the result is the same softmax.
-        float mx = -INFINITY;
+        // row max as a shallow tree (independent max3 operations, depth 4)
+        float m1[11];
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb2][j]);
+        for (int i = 0; i < 10; ++i) {
+            const int e = 3 * i;
+            m1[i] = fmaxf(fmaxf(s[e >> 4][e & 15], s[(e + 1) >> 4][(e + 1) & 15]),
+                          s[(e + 2) >> 4][(e + 2) & 15]);
+        }
+        m1[10] = fmaxf(s[1][14], s[1][15]);
+        const float m2a = fmaxf(fmaxf(m1[0], m1[1]), m1[2]);
+        const float m2b = fmaxf(fmaxf(m1[3], m1[4]), m1[5]);
+        const float m2c = fmaxf(fmaxf(m1[6], m1[7]), m1[8]);
+        const float m2d = fmaxf(m1[9], m1[10]);
+        float mx = fmaxf(fmaxf(m2a, m2b), fmaxf(m2c, m2d));
         mx = max_xor32(mx) * scale_log2;
         if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
             const float m_new = fmaxf(m_run, mx);
@@ -411,17 +420,32 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
             m_run = m_new;
         }
         const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-        float psum = 0.0f;
+        // p = 2^(s scale - m) in stages (all scalings, all exponentials, then
+        // the bf16 pairs and a tree row sum), pinned so that every dependent
+        // pair of instructions is far apart and no latency is exposed
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s[kb2][j] = s[kb2][j] * scale_log2 - m_use;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s[kb2][j] = fast_exp2(s[kb2][j]);
+        __builtin_amdgcn_sched_barrier(0);
+        float q1[16];
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
             for (int j = 0; j < 16; j += 2) {
-                float e0 = fast_exp2(s[kb2][j] * scale_log2 - m_use);
-                float e1 = fast_exp2(s[kb2][j + 1] * scale_log2 - m_use);
-                psum += e0 + e1;
-                pk[kb2][j / 2] = pack_bf16x2(e0, e1);
+                pk[kb2][j / 2] = pack_bf16x2(s[kb2][j], s[kb2][j + 1]);
+                q1[kb2 * 8 + j / 2] = s[kb2][j] + s[kb2][j + 1];
             }
-        l_run += psum;
+#pragma unroll
+        for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+            for (int i = 0; i < w; ++i) q1[i] = q1[i] + q1[i + w];
+        l_run += q1[0];
     };
 
     // ---- phases.  Even phase 2j: wait for this wave's copies, barrier, then
