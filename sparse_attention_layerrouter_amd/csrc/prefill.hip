@@ -7,20 +7,24 @@
 // blocks are visited [thelatestinai paper page, Table 6], so their KV tiles
 // are two contiguous runs and every skipped tile is never loaded.
 //
-// bf16 kernel (head_dim 128 or 64): one workgroup of 4 wavefronts owns 128
-// query rows that share one KV head (GQA stacking: 4 heads x 32 positions when
-// G >= 4), so every K/V tile staged in LDS serves 128 rows.  Per 64-key tile:
+// bf16 kernel (head_dim 128 or 64): one workgroup of 8 wavefronts owns 256
+// query rows that share one KV head (GQA stacking: 4 heads x 64 positions when
+// G >= 4), so every K/V tile staged in LDS serves 256 rows.  Per 64-key tile:
 //   S^T = K Q^T  on v_mfma_f32_32x32x16_bf16 (K from LDS, Q^T in registers);
 //   online softmax in the exp2 domain, row statistics per lane;
 //   O^T += V^T P^T on the same MFMA; P^T comes straight out of the S^T
 //   accumulators (no cross-lane movement) and V^T is read from the row-major
 //   V tile by the transposing LDS read ds_read_b64_tr_b16.
-// K and V tiles go global -> LDS directly (global_load_lds_dwordx4) into a
-// double buffer, each with a 16-byte XOR swizzle chosen so the MFMA operand
-// reads are bank-conflict free; the copy of tile i+1 is in flight while tile i
-// is computed.
-// The causal diagonal and the lower window edge are masked per element, all
-// other kept tiles run unmasked.
+// The 8 waves form two groups that ping-pong: while one group's softmax keeps
+// the vector ALUs busy, the other group's QK and PV products keep the matrix
+// cores of the same SIMDs busy (one wave of each group per SIMD); a single
+// wave cannot overlap the two itself, because its softmax depends on its own
+// QK and its PV on its own softmax.
+// K and V tiles go global -> LDS directly (buffer_load ... lds) into a double
+// buffer, each with a 16-byte XOR swizzle chosen so the MFMA operand reads are
+// bank-conflict free; the copies of the next tiles are in flight while the
+// current ones are computed.  The causal diagonal and the lower window edge
+// are masked per element, all other kept tiles run unmasked.
 //
 // Generic kernel (fp32, and bf16 shapes the MFMA kernel does not cover): one
 // thread per (query row, head), exact online softmax over the same kept
@@ -36,7 +40,7 @@ namespace {
 constexpr int kBN = 64;                // keys per KV tile
 constexpr int kWaves = 8;              // two ping-pong groups of 4 wavefronts
 constexpr int kThreads = 64 * kWaves;
-constexpr float kRescaleSlack = 8.0f;  // log2 units
+constexpr float kFastLimit = 65536.0f;  // largest p without a rescale
 
 // ---------------------------------------------------------------------------
 // LDS layout
@@ -391,61 +395,63 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                     if (!vis) s[kb2][j] = -INFINITY;
                 }
         }
-        // online softmax (exp2 domain) with a lazily moved reference max: the
-        // reference only moves when a row's tile max exceeds it by more than
-        // kRescaleSlack (log2 units), so p = 2^(s - m_ref) <= 2^kRescaleSlack and
-        // the O / l rescale runs on few tiles.  O / l does not depend on the
-        // reference, so the result is the same softmax.
-        // row max as a shallow tree (independent max3 operations, depth 4)
-        float m1[11];
+        // online softmax (exp2 domain) against a lazily moved reference m_ref.
+        // Fast path: p = 2^(s scale - m_ref) with the current reference; the
+        // lane's partial row sum bounds every p it holds, so if no lane's sum
+        // exceeds kFastLimit (and every row has a reference) nothing overflows
+        // and no rescale is needed.  Otherwise (rare: the first visible tile of
+        // a row, or scores that grew by many octaves) the tile max moves the
+        // reference, O and l are rescaled and p is recomputed.  O / l does not
+        // depend on the reference, so the result is the same softmax.
+        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
 #pragma unroll
-        for (int i = 0; i < 10; ++i) {
-            const int e = 3 * i;
-            m1[i] = fmaxf(fmaxf(s[e >> 4][e & 15], s[(e + 1) >> 4][(e + 1) & 15]),
-                          s[(e + 2) >> 4][(e + 2) & 15]);
-        }
-        m1[10] = fmaxf(s[1][14], s[1][15]);
-        const float m2a = fmaxf(fmaxf(m1[0], m1[1]), m1[2]);
-        const float m2b = fmaxf(fmaxf(m1[3], m1[4]), m1[5]);
-        const float m2c = fmaxf(fmaxf(m1[6], m1[7]), m1[8]);
-        const float m2d = fmaxf(m1[9], m1[10]);
-        float mx = fmaxf(fmaxf(m2a, m2b), fmaxf(m2c, m2d));
-        mx = max_xor32(mx) * scale_log2;
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s[kb2][j] = s[kb2][j] * scale_log2 - m_use;
+        __builtin_amdgcn_sched_barrier(0);
+        float e[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) e[i] = fast_exp2(s[i >> 4][i & 15]);
+        __builtin_amdgcn_sched_barrier(0);
+        auto row_sum = [&]() __attribute__((always_inline)) {
+            float q1[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) q1[i] = e[2 * i] + e[2 * i + 1];
+#pragma unroll
+            for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+                for (int i = 0; i < w; ++i) q1[i] = q1[i] + q1[i + w];
+            return q1[0];
+        };
+        float psum = row_sum();
+        const bool fast = m_run != -INFINITY && psum <= kFastLimit;  // NaN: not fast
+        if (__builtin_amdgcn_ballot_w64(!fast) != 0) {
+            float m1[11];
+#pragma unroll
+            for (int i = 0; i < 10; ++i) {
+                const int q = 3 * i;
+                m1[i] = fmaxf(fmaxf(s[q >> 4][q & 15], s[(q + 1) >> 4][(q + 1) & 15]),
+                              s[(q + 2) >> 4][(q + 2) & 15]);
+            }
+            m1[10] = fmaxf(s[1][14], s[1][15]);
+            float mx = fmaxf(fmaxf(fmaxf(m1[0], m1[1]), fmaxf(m1[2], m1[3])),
+                             fmaxf(fmaxf(m1[4], m1[5]), fmaxf(m1[6], m1[7])));
+            mx = fmaxf(mx, fmaxf(fmaxf(m1[8], m1[9]), m1[10]));
+            mx = max_xor32(mx) + m_use;   // tile max in the log2 domain
             const float m_new = fmaxf(m_run, mx);
             const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.0f : m_new));
             l_run *= alpha;
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
             m_run = m_new;
+            const float shift = m_use - (m_run == -INFINITY ? 0.0f : m_run);
+#pragma unroll
+            for (int i = 0; i < 32; ++i) e[i] = fast_exp2(s[i >> 4][i & 15] + shift);
+            psum = row_sum();
         }
-        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-        // p = 2^(s scale - m) in stages (all scalings, all exponentials, then
-        // the bf16 pairs and a tree row sum), pinned so that every dependent
-        // pair of instructions is far apart and no latency is exposed
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) s[kb2][j] = s[kb2][j] * scale_log2 - m_use;
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) s[kb2][j] = fast_exp2(s[kb2][j]);
-        __builtin_amdgcn_sched_barrier(0);
-        float q1[16];
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int j = 0; j < 16; j += 2) {
-                pk[kb2][j / 2] = pack_bf16x2(s[kb2][j], s[kb2][j + 1]);
-                q1[kb2 * 8 + j / 2] = s[kb2][j] + s[kb2][j + 1];
-            }
-#pragma unroll
-        for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-            for (int i = 0; i < w; ++i) q1[i] = q1[i] + q1[i + w];
-        l_run += q1[0];
+        for (int i = 0; i < 16; ++i) pk[i >> 3][i & 7] = pack_bf16x2(e[2 * i], e[2 * i + 1]);
+        l_run += psum;
     };
 
     // ---- phases.  Even phase 2j: wait for this wave's copies, barrier, then
@@ -481,6 +487,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
             else block_mfma(ic<0>{}, k_lds1, v_lds0, t0 + 1, nullptr, nullptr);
         }
     };
+    // Use the scale once before the loop: its scalar load is then known to have
+    // landed, so the LDS waits inside the loop count LDS reads only (a pending
+    // scalar load forces a full lgkmcnt(0) wait before every MFMA block).
+    asm volatile("" ::"s"(scale_log2));
     if (grp == 0) run(ic<0>{});
     else run(ic<1>{});
     // the last even phase issued copies nobody reads: let them land before the

@@ -203,6 +203,28 @@ def test_prefill_deterministic_and_sa_full_window_equals_fa():
     assert np.array_equal(a, c) and np.array_equal(la, lc)
 
 
+@pytest.mark.parametrize("bit", [1, 0])
+def test_prefill_bf16_rescale_path_growing_scores(bit):
+    """Key norms that grow 300x along the sequence make each row's scores climb
+    by many octaves from tile to tile, so the softmax reference max has to move
+    on many tiles (the rescale path, not only the first visible tile)."""
+    rng = np.random.default_rng(31)
+    T, hq, hkv, d = 1500, 8, 2, 128
+    cu = synth.cu_seqlens_of([T])
+    qf = rng.standard_normal((T, hq, d)).astype(np.float32)
+    kf = rng.standard_normal((T, hkv, d)).astype(np.float32)
+    kf *= (0.05 + np.arange(T, dtype=np.float32) / 100.0)[:, None, None]
+    vf = rng.standard_normal((T, hkv, d)).astype(np.float32)
+    q, k, v = (synth.f32_to_bf16_bits(a) for a in (qf, kf, vf))
+    route = np.full((1, 1), bit, np.uint8)
+    scale = 1 / math.sqrt(d)
+    o, lse = run_prefill(q, k, v, cu, route, 0, 64, 256, 64, scale)
+    o_ref, l_ref = oracle.attn_prefill(q, k, v, cu, route, 0, 64, 256, 64, scale)
+    assert np.abs(l_ref).max() > 20.0  # the scores really are large
+    assert max_err(o, o_ref) <= TOL_BF16
+    assert np.abs(lse - l_ref).max() <= TOL_LSE
+
+
 # ---------------------------------------------------------------------------
 # Decode
 # ---------------------------------------------------------------------------
