@@ -9,7 +9,9 @@ sparse_attention_layerrouter_amd/libfluxattn.so.
 from __future__ import annotations
 
 import concurrent.futures
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -30,23 +32,58 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 SOURCES = ["router.hip", "prefill.hip", "decode.hip", "api.cpp"]
+# The hot MFMA / split-K kernels keep everything in registers: a build whose
+# compiler places any of their state in scratch memory (spills or a stack
+# array) is refused, since it would run many times slower.
+HOT_KERNELS = ("prefill_bf16_kernel", "decode_bf16_kernel", "decode_split_kernel")
+_REMARK = re.compile(r"remark:\s+(Function Name|ScratchSize \[bytes/lane\]|VGPRs Spill|VGPRs|AGPRs"
+                     r"|LDS Size \[bytes/block\]|Occupancy \[waves/SIMD\]):\s+(\S+)")
 
 
-def _compile(src: str) -> str:
+def _resources(stderr: str) -> dict:
+    """{kernel symbol: {field: value}} from -Rpass-analysis=kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for m in _REMARK.finditer(stderr):
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[key] = int(val) if val.lstrip("-").isdigit() else val
+    return out
+
+
+def _compile(src: str):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
+    else:
+        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
-    return obj
+    return obj, _resources(r.stderr)
+
+
+def check_resources(res: dict) -> None:
+    bad = [f"{k}: scratch {v.get('ScratchSize [bytes/lane]')} B/lane, "
+           f"{v.get('VGPRs Spill')} VGPR spills"
+           for k, v in res.items()
+           if any(h in k for h in HOT_KERNELS)
+           and (v.get("ScratchSize [bytes/lane]", 0) != 0 or v.get("VGPRs Spill", 0) != 0)]
+    if bad:
+        raise RuntimeError("hot kernels would use scratch memory:\n  " + "\n  ".join(bad))
 
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        done = list(ex.map(_compile, SOURCES))
+    objs = [o for o, _ in done]
+    res = {k: v for _, r in done for k, v in r.items()}
+    with open(os.path.join(BUILD_DIR, "kernel_resources.json"), "w") as f:
+        json.dump(res, f, indent=1, sort_keys=True)
+    check_resources(res)
     tmp = OUT + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
