@@ -24,8 +24,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 HOT_KERNELS = {
     "prefill_bf16_fa_131k": ("prefill_bf16_kernel<128, 1>", ("prefill.hip", "fa_common.h")),
     "prefill_bf16_sa_131k": ("prefill_bf16_kernel<128, 2>", ("prefill.hip", "fa_common.h")),
-    "decode_bf16_fa_131k": ("decode_bf16_kernel<128, 4, 1>", ("decode.hip", "fa_common.h")),
-    "decode_bf16_sa_131k": ("decode_bf16_kernel<128, 4, 2>", ("decode.hip", "fa_common.h")),
+    "decode_bf16_fa_131k": ("decode_bf16_kernel<128, 4, 1, false>", ("decode.hip", "fa_common.h")),
+    "decode_bf16_sa_131k": ("decode_bf16_kernel<128, 4, 2, false>", ("decode.hip", "fa_common.h")),
 }
 COPY_BYTES = 1 << 30
 
