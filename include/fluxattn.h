@@ -174,6 +174,36 @@ fa_status fa_attn_prefill(const void *q, const void *k, const void *v, void *o,
                           int32_t window_tokens, int32_t block_tokens,
                           float sm_scale, void *stream);
 
+/*
+ * fa_attn_prefill_kv -- prefill of the last Tq_b tokens of each sequence whose
+ * keys and values hold all Tk_b >= Tq_b of its tokens: chunked prefill (the
+ * pages run prefill in chunks of 16384 tokens, [thelatestinai paper page,
+ * Table 6]) and prefill appended to a cached prefix.  Query row i of sequence
+ * b sits at absolute position Tk_b - Tq_b + i; the masks, the route and every
+ * output are those of fa_attn_prefill on the whole sequence, restricted to
+ * these rows.  fa_attn_prefill is the case cu_seqlens_q = cu_seqlens_k.
+ *
+ * q [total_q][n_q_heads][head_dim], o [total_q][n_q_heads][head_dim] out,
+ * lse [total_q][n_q_heads] fp32 out (nullable), total_q = cu_seqlens_q[batch];
+ * k, v [total_k][n_kv_heads][head_dim], total_k = cu_seqlens_k[batch].
+ * cu_seqlens_q, cu_seqlens_k [batch + 1] int32 device.
+ * max_seqlen_q: host upper bound of every Tq_b (sizes the grid).
+ * Other arguments, kernels and support as fa_attn_prefill.
+ * Device behaviour: a sequence with Tq_b > Tk_b reads nothing and gets NaN
+ * outputs.
+ * Errors: as fa_attn_prefill (cu_seqlens_k NULL -> FA_ERR_INVALID_ARG).
+ */
+fa_status fa_attn_prefill_kv(const void *q, const void *k, const void *v, void *o,
+                             float *lse, int32_t dtype,
+                             const int32_t *cu_seqlens_q,
+                             const int32_t *cu_seqlens_k, int32_t batch,
+                             int32_t max_seqlen_q, int32_t n_q_heads,
+                             int32_t n_kv_heads, int32_t head_dim,
+                             const uint8_t *route, const uint8_t *route_host,
+                             int32_t n_layers, int32_t layer, int32_t sink_tokens,
+                             int32_t window_tokens, int32_t block_tokens,
+                             float sm_scale, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Decode attention                                                         */
 /* ------------------------------------------------------------------------ */

@@ -22,7 +22,7 @@ FA_F32, FA_BF16 = 0, 1
 EXPORTS = (
     "fa_last_error", "fa_abi_version", "fa_router_workspace_size", "fa_router_decide",
     "fa_block_plan", "fa_attn_prefill", "fa_decode_workspace_size", "fa_attn_decode",
-    "fa_kv_compact", "fa_attn_decode_ring",
+    "fa_kv_compact", "fa_attn_decode_ring", "fa_attn_prefill_kv",
 )
 
 
@@ -58,6 +58,9 @@ def lib() -> ctypes.CDLL:
     L.fa_attn_prefill.restype = I32
     L.fa_attn_prefill.argtypes = [P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, P, P, I32,
                                   I32, I32, I32, I32, F, P]
+    L.fa_attn_prefill_kv.restype = I32
+    L.fa_attn_prefill_kv.argtypes = [P, P, P, P, P, I32, P, P, I32, I32, I32, I32, I32, P, P,
+                                     I32, I32, I32, I32, I32, F, P]
     L.fa_decode_workspace_size.restype = SZ
     L.fa_decode_workspace_size.argtypes = [I32, I32, I32, I32]
     L.fa_attn_decode.restype = I32
@@ -178,6 +181,24 @@ def fa_attn_prefill(q, k, v, o, cu_seqlens, max_seqlen, route, layer, sink_token
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dtype_code(q), _ptr(cu_seqlens), batch,
         int(max_seqlen), hq, hkv, d, _ptr(route), rh, route.shape[1], layer, sink_tokens,
         window_tokens, block_tokens, float(sm_scale), _stream(stream)))
+    del keep
+
+
+def fa_attn_prefill_kv(q, k, v, o, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, route, layer,
+                       sink_tokens, window_tokens, block_tokens, sm_scale, lse=None,
+                       route_host=None, stream=None):
+    """Prefill of the last Tq tokens of each sequence against all Tk of its keys:
+    q [total_q, Hq, d], k/v [total_k, Hkv, d] -> o [total_q, Hq, d]."""
+    _require_cuda(q, k, v, o, cu_seqlens_q, cu_seqlens_k, route, lse)
+    batch = cu_seqlens_q.numel() - 1
+    _, hq, d = q.shape
+    hkv = k.shape[1]
+    keep, rh = _host_u8(route_host)
+    _check(lib().fa_attn_prefill_kv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dtype_code(q), _ptr(cu_seqlens_q),
+        _ptr(cu_seqlens_k), batch, int(max_seqlen_q), hq, hkv, d, _ptr(route), rh,
+        route.shape[1], layer, sink_tokens, window_tokens, block_tokens, float(sm_scale),
+        _stream(stream)))
     del keep
 
 

@@ -79,13 +79,63 @@ size_t decode_splits_cap(int max_cache)
     return (size_t)(s > 64 ? s : 64);
 }
 
+// Shared by fa_attn_prefill (queries = keys) and fa_attn_prefill_kv.
+fa_status prefill_impl(const char *fn, const void *q, const void *k, const void *v, void *o,
+                       float *lse, int32_t dtype, const int32_t *cu_q, const int32_t *cu_k,
+                       int32_t batch, int32_t max_seqlen, int32_t n_q_heads, int32_t n_kv_heads,
+                       int32_t head_dim, const uint8_t *route, const uint8_t *route_host,
+                       int32_t n_layers, int32_t layer, int32_t sink_tokens,
+                       int32_t window_tokens, int32_t block_tokens, float sm_scale, void *stream)
+{
+    if (!q || !k || !v || !o || !cu_q || !route)
+        return fail(FA_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    if (batch <= 0 || max_seqlen <= 0)
+        return fail(FA_ERR_INVALID_ARG, "%s: batch=%d max_seqlen=%d must be positive", fn, batch,
+                    max_seqlen);
+    if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0)
+        return fail(FA_ERR_INVALID_ARG,
+                    "%s: n_q_heads=%d must be a positive multiple of n_kv_heads=%d", fn,
+                    n_q_heads, n_kv_heads);
+    if (n_layers <= 0 || layer < 0 || layer >= n_layers)
+        return fail(FA_ERR_INVALID_ARG, "%s: layer %d outside [0, %d)", fn, layer, n_layers);
+    if (!std::isfinite(sm_scale) || sm_scale <= 0.0f)
+        return fail(FA_ERR_INVALID_ARG, "%s: sm_scale must be finite and > 0", fn);
+    fa::PrefillArgs a{};
+    if (!sparse_cfg(sink_tokens, window_tokens, block_tokens, a.ns, a.nw, a.bk_log2))
+        return fail(FA_ERR_INVALID_ARG, "%s: bad sparse config sink=%d window=%d block=%d", fn,
+                    sink_tokens, window_tokens, block_tokens);
+    if (dtype != FA_F32 && dtype != FA_BF16)
+        return fail(FA_ERR_UNSUPPORTED, "%s: dtype %d is not FA_F32/FA_BF16", fn, dtype);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", fn, head_dim);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.bf16 = dtype == FA_BF16;
+    a.cu_seqlens = cu_q;
+    a.cu_seqlens_k = cu_k;
+    a.batch = batch;
+    a.max_seqlen = max_seqlen;
+    a.hq = n_q_heads;
+    a.hkv = n_kv_heads;
+    a.d = head_dim;
+    a.route = route;
+    a.n_layers = n_layers;
+    a.layer = layer;
+    a.sm_scale = sm_scale;
+    a.mode = route_mode(route_host, batch, n_layers, layer);
+    return hip_status(fa::launch_prefill(a, (hipStream_t)stream), fn);
+}
+
 }  // namespace
 
 extern "C" {
 
 const char *fa_last_error(void) { return g_last_error.c_str(); }
 
-int32_t fa_abi_version(void) { return 3; }
+int32_t fa_abi_version(void) { return 4; }
 
 size_t fa_router_workspace_size(int32_t batch, int32_t hidden, int32_t router_hidden)
 {
@@ -169,47 +219,25 @@ fa_status fa_attn_prefill(const void *q, const void *k, const void *v, void *o, 
                           int32_t window_tokens, int32_t block_tokens, float sm_scale,
                           void *stream)
 {
-    if (!q || !k || !v || !o || !cu_seqlens || !route)
-        return fail(FA_ERR_INVALID_ARG, "fa_attn_prefill: a required pointer is NULL");
-    if (batch <= 0 || max_seqlen <= 0)
-        return fail(FA_ERR_INVALID_ARG, "fa_attn_prefill: batch=%d max_seqlen=%d must be positive",
-                    batch, max_seqlen);
-    if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0)
-        return fail(FA_ERR_INVALID_ARG,
-                    "fa_attn_prefill: n_q_heads=%d must be a positive multiple of n_kv_heads=%d",
-                    n_q_heads, n_kv_heads);
-    if (n_layers <= 0 || layer < 0 || layer >= n_layers)
-        return fail(FA_ERR_INVALID_ARG, "fa_attn_prefill: layer %d outside [0, %d)", layer,
-                    n_layers);
-    if (!std::isfinite(sm_scale) || sm_scale <= 0.0f)
-        return fail(FA_ERR_INVALID_ARG, "fa_attn_prefill: sm_scale must be finite and > 0");
-    fa::PrefillArgs a{};
-    if (!sparse_cfg(sink_tokens, window_tokens, block_tokens, a.ns, a.nw, a.bk_log2))
-        return fail(FA_ERR_INVALID_ARG,
-                    "fa_attn_prefill: bad sparse config sink=%d window=%d block=%d", sink_tokens,
-                    window_tokens, block_tokens);
-    if (dtype != FA_F32 && dtype != FA_BF16)
-        return fail(FA_ERR_UNSUPPORTED, "fa_attn_prefill: dtype %d is not FA_F32/FA_BF16", dtype);
-    if (head_dim != 64 && head_dim != 128)
-        return fail(FA_ERR_UNSUPPORTED, "fa_attn_prefill: head_dim %d not in {64, 128}", head_dim);
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.o = o;
-    a.lse = lse;
-    a.bf16 = dtype == FA_BF16;
-    a.cu_seqlens = cu_seqlens;
-    a.batch = batch;
-    a.max_seqlen = max_seqlen;
-    a.hq = n_q_heads;
-    a.hkv = n_kv_heads;
-    a.d = head_dim;
-    a.route = route;
-    a.n_layers = n_layers;
-    a.layer = layer;
-    a.sm_scale = sm_scale;
-    a.mode = route_mode(route_host, batch, n_layers, layer);
-    return hip_status(fa::launch_prefill(a, (hipStream_t)stream), "fa_attn_prefill");
+    return prefill_impl("fa_attn_prefill", q, k, v, o, lse, dtype, cu_seqlens, cu_seqlens, batch,
+                        max_seqlen, n_q_heads, n_kv_heads, head_dim, route, route_host, n_layers,
+                        layer, sink_tokens, window_tokens, block_tokens, sm_scale, stream);
+}
+
+fa_status fa_attn_prefill_kv(const void *q, const void *k, const void *v, void *o, float *lse,
+                             int32_t dtype, const int32_t *cu_seqlens_q,
+                             const int32_t *cu_seqlens_k, int32_t batch, int32_t max_seqlen_q,
+                             int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                             const uint8_t *route, const uint8_t *route_host, int32_t n_layers,
+                             int32_t layer, int32_t sink_tokens, int32_t window_tokens,
+                             int32_t block_tokens, float sm_scale, void *stream)
+{
+    if (!cu_seqlens_k)
+        return fail(FA_ERR_INVALID_ARG, "fa_attn_prefill_kv: a required pointer is NULL");
+    return prefill_impl("fa_attn_prefill_kv", q, k, v, o, lse, dtype, cu_seqlens_q, cu_seqlens_k,
+                        batch, max_seqlen_q, n_q_heads, n_kv_heads, head_dim, route, route_host,
+                        n_layers, layer, sink_tokens, window_tokens, block_tokens, sm_scale,
+                        stream);
 }
 
 size_t fa_decode_workspace_size(int32_t batch, int32_t n_q_heads, int32_t head_dim,

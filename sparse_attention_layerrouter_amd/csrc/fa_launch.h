@@ -47,8 +47,9 @@ struct PrefillArgs {
     void *o;
     float *lse;
     int bf16;
-    const int32_t *cu_seqlens;
-    int batch, max_seqlen, hq, hkv, d;
+    const int32_t *cu_seqlens;    // query rows of each sequence
+    const int32_t *cu_seqlens_k;  // key rows (the queries are the last rows of the keys)
+    int batch, max_seqlen, hq, hkv, d;  // max_seqlen bounds the query rows
     const uint8_t *route;
     int n_layers, layer;
     int ns, nw, bk_log2;

@@ -145,7 +145,8 @@ template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
-    const int32_t *__restrict__ cu, const uint8_t *__restrict__ route, int n_layers, int layer,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ cu_k,
+    const uint8_t *__restrict__ route, int n_layers, int layer,
     int hq, int hkv, int G, int hpw, int n_hgroups, int n_units, int n_ptiles,
     SparseRule rule, float scale_log2)
 {
@@ -177,18 +178,34 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int ptile = n_ptiles - 1 - bid / n_hgroups;
     const int b = unit / hkv, kvh = unit % hkv;
 
-    const int start = cu[b];
-    const int T = cu[b + 1] - start;
+    // Query rows of sequence b are cu[b] .. cu[b+1]-1 and its keys cu_k[b] ..
+    // cu_k[b+1]-1; the Tq queries are the last Tq of the T tokens, so query row
+    // r sits at position q_off + r (q_off = 0 when queries and keys coincide).
+    const int start_q = cu[b];
+    const int Tq = cu[b + 1] - start_q;
+    const int start = cu_k[b];
+    const int T = cu_k[b + 1] - start;
+    const int q_off = T - Tq;
     const int wph = 4 / hpw;        // waves per head in a group
     const int gpos = 32 * wph;      // positions per group
-    const int p0 = ptile * 2 * gpos;
-    if (p0 >= T) return;            // uniform: the whole workgroup leaves
+    const int r0 = ptile * 2 * gpos;
+    if (r0 >= Tq) return;           // uniform: the whole workgroup leaves
+    const int h = kvh * G + hg * hpw + wq / wph;
+    if (q_off < 0) {                // more queries than keys: NaN rows, nothing read
+        const int r = r0 + grp * gpos + (wq % wph) * 32 + l32;
+        if (r < Tq) {
+            uint16_t *orow = o + ((size_t)(start_q + r) * hq + h) * D;
+            for (int d = half; d < D; d += 2) orow[d] = 0x7fc0u;
+            if (lse && half == 0) lse[(size_t)(start_q + r) * hq + h] = __builtin_nanf("");
+        }
+        return;
+    }
+    const int p0 = q_off + r0;      // positions of this workgroup: p0 .. p1-1
     const int p1 = min(p0 + 2 * gpos, T);
     const bool is_fa = MODE == kModeFA ? true
                        : MODE == kModeSA ? false
                                          : route[(size_t)b * n_layers + layer] != 0;
 
-    const int h = kvh * G + hg * hpw + wq / wph;
     const int pw0 = p0 + grp * gpos + (wq % wph) * 32;  // this wave's first position
     const bool wave_active = pw0 < T;
     const int pw_last = min(pw0 + 31, T - 1);  // last valid position of the wave
@@ -229,8 +246,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // ---- Q^T operand in registers: lane holds row pw0 + l32, d = ks*16 + half*8 ..
     bf16x8 qreg[D / 16];
     {
-        int t = min(pw0 + l32, T - 1);
-        const uint16_t *qr = q + ((size_t)(start + t) * hq + h) * D;
+        const int t = min(pw0 + l32, T - 1);
+        const uint16_t *qr = q + ((size_t)(start_q + t - q_off) * hq + h) * D;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
             qreg[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qr + ks * 16 + half * 8));
@@ -503,7 +520,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const int t = pw0 + l32;
     if (t < T) {
-        uint16_t *orow = o + ((size_t)(start + t) * hq + h) * D;
+        const size_t row = (size_t)(start_q + t - q_off);
+        uint16_t *orow = o + (row * hq + h) * D;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -513,8 +531,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                            pack_bf16x2(oacc[dt][4 * jg + 2] * inv, oacc[dt][4 * jg + 3] * inv)};
                 *(u32x2 *)(orow + d) = w;
             }
-        if (lse && half == 0)
-            lse[(size_t)(start + t) * hq + h] = (m_run + fast_log2(l_tot)) * kLn2;
+        if (lse && half == 0) lse[row * hq + h] = (m_run + fast_log2(l_tot)) * kLn2;
     }
 }
 
@@ -534,15 +551,32 @@ template <typename TE, int D, int MODE>
 __global__ __launch_bounds__(64) void prefill_generic_kernel(
     const TE *__restrict__ q, const TE *__restrict__ k, const TE *__restrict__ v,
     TE *__restrict__ o, float *__restrict__ lse, const int32_t *__restrict__ cu,
-    const uint8_t *__restrict__ route, int n_layers, int layer, int hq, int hkv,
-    SparseRule rule, float scale_log2)
+    const int32_t *__restrict__ cu_k, const uint8_t *__restrict__ route, int n_layers,
+    int layer, int hq, int hkv, SparseRule rule, float scale_log2)
 {
     const int b = blockIdx.z;
     const int h = blockIdx.y;
-    const int start = cu[b];
-    const int T = cu[b + 1] - start;
-    const int p0 = blockIdx.x * 64;
-    if (p0 >= T) return;
+    // query rows cu[b] .., keys cu_k[b] ..; query row r sits at position q_off + r
+    const int start_q = cu[b];
+    const int Tq = cu[b + 1] - start_q;
+    const int start = cu_k[b];
+    const int T = cu_k[b + 1] - start;
+    const int q_off = T - Tq;
+    const int r0 = blockIdx.x * 64;
+    if (r0 >= Tq) return;
+    if (q_off < 0) {  // more queries than keys: NaN rows, nothing read
+        const int r = r0 + (int)threadIdx.x;
+        if (r < Tq) {
+            TE *orow = o + ((size_t)(start_q + r) * hq + h) * D;
+            for (int c = 0; c < D; ++c) {
+                if constexpr (sizeof(TE) == 2) ((uint16_t *)orow)[c] = 0x7fc0u;
+                else ((float *)orow)[c] = __builtin_nanf("");
+            }
+            if (lse) lse[(size_t)(start_q + r) * hq + h] = __builtin_nanf("");
+        }
+        return;
+    }
+    const int p0 = q_off + r0;
     const int p1 = min(p0 + 64, T);
     const int t = min(p0 + (int)threadIdx.x, T - 1);
     const bool is_fa = MODE == kModeFA ? true
@@ -552,7 +586,7 @@ __global__ __launch_bounds__(64) void prefill_generic_kernel(
     const int g = h / G;
 
     float qv[D], acc[D];
-    const TE *qr = q + ((size_t)(start + t) * hq + h) * D;
+    const TE *qr = q + ((size_t)(start_q + t - q_off) * hq + h) * D;
 #pragma unroll
     for (int c = 0; c < D; ++c) {
         qv[c] = ld_elem<TE, D>(qr, c) * scale_log2;
@@ -582,7 +616,8 @@ __global__ __launch_bounds__(64) void prefill_generic_kernel(
     }
     if (p0 + (int)threadIdx.x >= T) return;
     const float inv = 1.0f / l;
-    TE *orow = o + ((size_t)(start + t) * hq + h) * D;
+    const size_t row = (size_t)(start_q + t - q_off);
+    TE *orow = o + (row * hq + h) * D;
 #pragma unroll
     for (int c = 0; c < D; ++c) {
         if constexpr (sizeof(TE) == 2)
@@ -590,7 +625,7 @@ __global__ __launch_bounds__(64) void prefill_generic_kernel(
         else
             ((float *)orow)[c] = acc[c] * inv;
     }
-    if (lse) lse[(size_t)(start + t) * hq + h] = (m + fast_log2(l)) * kLn2;
+    if (lse) lse[row * hq + h] = (m + fast_log2(l)) * kLn2;
 }
 
 template <typename TE, int D, int MODE>
@@ -600,7 +635,7 @@ hipError_t launch_generic(const PrefillArgs &a, hipStream_t stream, const Sparse
     dim3 grid((a.max_seqlen + 63) / 64, a.hq, a.batch);
     prefill_generic_kernel<TE, D, MODE><<<grid, 64, 0, stream>>>(
         (const TE *)a.q, (const TE *)a.k, (const TE *)a.v, (TE *)a.o, a.lse, a.cu_seqlens,
-        a.route, a.n_layers, a.layer, a.hq, a.hkv, r, scale_log2);
+        a.cu_seqlens_k, a.route, a.n_layers, a.layer, a.hq, a.hkv, r, scale_log2);
     return hipGetLastError();
 }
 
@@ -618,8 +653,8 @@ hipError_t launch_mfma(const PrefillArgs &a, hipStream_t stream, const SparseRul
     if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     prefill_bf16_kernel<D, MODE><<<(unsigned)n_wg, kThreads, 0, stream>>>(
         (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, (uint16_t *)a.o,
-        a.lse, a.cu_seqlens, a.route, a.n_layers, a.layer, a.hq, a.hkv, G, hpw, n_hgroups,
-        n_units, n_ptiles, r, scale_log2);
+        a.lse, a.cu_seqlens, a.cu_seqlens_k, a.route, a.n_layers, a.layer, a.hq, a.hkv, G, hpw,
+        n_hgroups, n_units, n_ptiles, r, scale_log2);
     return hipGetLastError();
 }
 

@@ -27,14 +27,14 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     assert set(names) == set(_lib.EXPORTS)
     for name in names:
         assert hasattr(L, name), name
 
 
 def test_abi_version_and_clean_error_state():
-    assert _lib.fa_abi_version() == 3
+    assert _lib.fa_abi_version() == 4
 
 
 def test_workspace_sizes():
@@ -80,6 +80,25 @@ def prefill_args(**kw):
 def test_prefill_validation(kw, status):
     assert _lib.lib().fa_attn_prefill(*prefill_args(**kw)) == status
     assert _lib.last_error().startswith("fa_attn_prefill")
+
+
+def prefill_kv_args(cu_k=P, **kw):
+    a = prefill_args(**kw)
+    return a[:7] + [cu_k] + a[7:]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu_k=None), _lib.FA_ERR_INVALID_ARG),
+    (dict(cu=None), _lib.FA_ERR_INVALID_ARG),
+    (dict(max_seqlen=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(hq=30, hkv=8), _lib.FA_ERR_INVALID_ARG),
+    (dict(layer=2), _lib.FA_ERR_INVALID_ARG),
+    (dict(sink=100), _lib.FA_ERR_INVALID_ARG),
+    (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
+])
+def test_prefill_kv_validation(kw, status):
+    assert _lib.lib().fa_attn_prefill_kv(*prefill_kv_args(**kw)) == status
+    assert _lib.last_error().startswith("fa_attn_prefill_kv")
 
 
 def decode_args(**kw):
