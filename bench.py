@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--no-sweep", action="store_true", help="skip the 8k/32k/64k prefill sweep")
     p.add_argument("--no-serving", action="store_true",
                    help="skip the batched decode sweep (batch 8/16/24/32 at a 32K context)")
+    p.add_argument("--no-chunked", action="store_true",
+                   help="skip the chunked prefill (16384-token chunks over a growing key prefix)")
     p.add_argument("--cpu-rows", type=int, default=192,
                    help="query rows of the FA layer the oracle times (SA gets 4x)")
     p.add_argument("--profile", action="store_true",
@@ -248,6 +250,7 @@ def main():
     wall = time.perf_counter() - t0
     log(f"timed {args.steps} steps in {wall:.2f} s")
 
+    route_full = route.clone()  # the sweeps below re-run the router on shorter inputs
     route_np = route.cpu().numpy()[0]
     logits_np = logits.cpu().numpy()[0]
     n_fa = int(route_np.sum())
@@ -417,13 +420,42 @@ def main():
                       "speedup_vs_all_fa": round(t_prefill_allfa / t_prefill, 3)})
         log("context sweep done")
 
+    # ---- chunked prefill: the same routed 32-layer prefill in 16384-token chunks,
+    # each chunk's queries against the whole key prefix (fa_attn_prefill_kv)
+    chunked = None
+    CHUNK = 16384
+    if not args.no_chunked and T % CHUNK == 0 and T > CHUNK:
+        r_host = route_full.cpu().numpy()
+        cu_q = torch.tensor([0, CHUNK], dtype=torch.int32, device=dev)
+        cu_ks = [torch.tensor([0, c1], dtype=torch.int32, device=dev)
+                 for c1 in range(CHUNK, T + 1, CHUNK)]
+        ms_pass = None
+        for rep in range(2):  # first pass warms up, second is timed
+            a, b_ = ev(), ev()
+            a.record(stream)
+            for ci, cu_k in enumerate(cu_ks):
+                c0, c1 = ci * CHUNK, (ci + 1) * CHUNK
+                for l in range(N_LAYERS):
+                    q, k, v = sets[l % n_sets]
+                    _lib.fa_attn_prefill_kv(q[c0:c1], k[:c1], v[:c1], o_pre[c0:c1], cu_q, cu_k,
+                                            CHUNK, route_full, l, SINK, WINDOW, BLOCK, scale,
+                                            route_host=r_host)
+            b_.record(stream)
+            torch.cuda.synchronize()
+            ms_pass = a.elapsed_time(b_)
+        t_chunked = ms_pass * 1e-3 + t_router
+        chunked = {"chunk": CHUNK, "tok_s": round(T / t_chunked, 1),
+                   "ms": round(t_chunked * 1e3, 3),
+                   "vs_one_call": round(t_prefill / t_chunked, 3)}
+        log("chunked prefill done")
+
     # ---- roofline --------------------------------------------------------------
     fa_flop = flops_of_pairs(pairs_fa(T))
     sa_flop = flops_of_pairs(pairs_sa(T))
     achieved_tflops = fa_flop / t_fa / 1e12
     pre_hash = source_hash("prefill.hip", "fa_common.h")
     dec_hash = source_hash("decode.hip", "fa_common.h")
-    traffic_pre = read_traffic("prefill_bf16_fa_32k", pre_hash)
+    traffic_pre = read_traffic("prefill_bf16_fa_131k", pre_hash)
     dec_bytes = NB * HKV * NC * D * 2 * 2 + 2 * NB * HQ * D * 2
     dec_sa_bytes = NB * HKV * kept_tokens_decode(NC, False) * D * 2 * 2 + 2 * NB * HQ * D * 2
     achieved_gbs = dec_bytes / td_fa / 1e9
@@ -461,6 +493,7 @@ def main():
             "all_fa_ms": round(t_prefill_allfa * 1e3, 3),
             "speedup_vs_all_fa": round(t_prefill_allfa / t_prefill, 3),
             "context_sweep": sweep,
+            "chunked_16k": chunked,
         },
         "decode": {
             "tok_s": round(NB / t_decode, 1),
