@@ -90,10 +90,13 @@ __global__ __launch_bounds__(256) void router_gemv1_kernel(const float *__restri
 }
 
 // logit[b][l] = sum_i W2[l][i] h[b][i] + b2[l]; route = logit > 0.
+// An empty sequence has no pooled vector: its logits are NaN and its bits SA.
 __global__ __launch_bounds__(256) void router_gemv2_kernel(const float *__restrict__ w2,
                                                            const float *__restrict__ b2,
-                                                           const float *__restrict__ h, int batch,
-                                                           int router_hidden, int n_layers,
+                                                           const float *__restrict__ h,
+                                                           const int32_t *__restrict__ cu,
+                                                           int batch, int router_hidden,
+                                                           int n_layers,
                                                            uint8_t *__restrict__ route,
                                                            float *__restrict__ logits)
 {
@@ -106,6 +109,7 @@ __global__ __launch_bounds__(256) void router_gemv2_kernel(const float *__restri
     float acc = 0.0f;
     for (int i = lane; i < router_hidden; i += 64) acc += wr[i] * hb[i];
     acc = wave_sum(acc) + b2[l];
+    if (cu[b + 1] - cu[b] <= 0) acc = __builtin_nanf("");
     if (lane == 0) {
         route[unit] = acc > 0.0f ? 1 : 0;  // NaN compares false -> SA
         if (logits) logits[unit] = acc;
@@ -151,7 +155,8 @@ hipError_t launch_router(const RouterArgs &a, hipStream_t stream)
     router_gemv1_kernel<<<(a.router_hidden + 3) / 4, 256, 0, stream>>>(
         a.w1, a.b1, a.ws_pool, a.batch, a.hidden, a.router_hidden, a.ws_hidden);
     router_gemv2_kernel<<<(a.batch * a.n_layers + 3) / 4, 256, 0, stream>>>(
-        a.w2, a.b2, a.ws_hidden, a.batch, a.router_hidden, a.n_layers, a.route, a.logits);
+        a.w2, a.b2, a.ws_hidden, a.cu_seqlens, a.batch, a.router_hidden, a.n_layers, a.route,
+        a.logits);
     return hipGetLastError();
 }
 

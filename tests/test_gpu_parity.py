@@ -225,6 +225,42 @@ def test_prefill_bf16_rescale_path_growing_scores(bit):
     assert np.abs(lse - l_ref).max() <= TOL_LSE
 
 
+def test_empty_sequence_in_varlen_batch():
+    """A zero-length sequence inside a varlen batch.  The router gives it route 0
+    and NaN logits (the documented device behaviour), its block-plan rows are
+    all (0, 0, 0, 0), prefill writes nothing for it, and every other sequence
+    matches the oracle run on the batch without it (the packed rows are the
+    same): route bits bit-exact, attention within the bf16 bar."""
+    rng = np.random.default_rng(44)
+    lengths, kept = [300, 0, 129], [300, 129]
+    cu, cu_kept = synth.cu_seqlens_of(lengths), synth.cu_seqlens_of(kept)
+    hidden, L = 256, 3
+    x = rng.standard_normal((int(cu[-1]), hidden)).astype(np.float32)
+    w1, b1, w2, b2 = synth.router_weights(rng, hidden, 16, L)
+    route, logits = run_router(x, cu, 64, w1, b1, w2, b2)
+    assert route[1].tolist() == [0] * L and np.isnan(logits[1]).all()
+    r_ref, _, l64 = oracle.router(x, cu_kept, 64, w1, b1, w2, b2)
+    assert np.abs(l64).min() > 1e-4
+    assert np.array_equal(route[[0, 2]], r_ref)
+
+    mq = 8
+    plan = torch.full((3, mq, 4), -7, dtype=torch.int32, device=DEV)
+    route_bits = np.array([[0], [1], [0]], np.uint8)
+    _lib.fa_block_plan(i32(cu), mq, u8(route_bits), 0, 64, 128, 64, plan)
+    torch.cuda.synchronize()
+    plan = plan.cpu().numpy()
+    assert not plan[1].any()
+    assert np.array_equal(plan, oracle.block_plan(lengths, mq, route_bits, 0, 64, 128, 64))
+
+    q, k, v = synth.qkv_host(rng, int(cu[-1]), 8, 2, 128, bf16=True)
+    scale = 1 / math.sqrt(128)
+    o, lse = run_prefill(q, k, v, cu, route_bits, 0, 64, 128, 64, scale)
+    o_ref, l_ref = oracle.attn_prefill(q, k, v, cu_kept, route_bits[[0, 2]], 0, 64, 128, 64,
+                                       scale)
+    assert max_err(o, o_ref) <= TOL_BF16
+    assert np.abs(lse - l_ref).max() <= TOL_LSE
+
+
 # ---------------------------------------------------------------------------
 # Decode
 # ---------------------------------------------------------------------------
