@@ -205,6 +205,60 @@ fa_status fa_attn_prefill_kv(const void *q, const void *k, const void *v, void *
                              float sm_scale, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* XAttention sparse branch                                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The pages name XAttention ("Block Sparse Attention with Antidiagonal
+ * Scoring", mlsanity page reference list) as a block-level sparse operator for
+ * prefill whose blocks are chosen by a selection score [thelatestinai paper
+ * page, Table 4 and Table 12]; the branch runs in three calls:
+ * fa_xattn_scores -> fa_xattn_select -> fa_attn_prefill_xattn.
+ *
+ * fa_xattn_scores -- antidiagonal block scores.  With stride S and block B =
+ * 16 S, reshaped query row a of a sequence stands for positions a*S + S-1-s and
+ * reshaped key row b for positions b*S + s (s = 0..S-1; positions past the
+ * sequence are zero vectors);
+ *   A[a][b] = (sm_scale / S) * sum_s <q[a*S+S-1-s][h], k[b*S+s][h/G]>  (b <= a),
+ *   P = softmax over b of A[a][.],
+ *   scores[b][h][i][j] = sum of P over the 16 reshaped rows of query block i
+ *                        and the 16 reshaped columns of key block j (j <= i).
+ * q [total][n_q_heads][head_dim], k [total][n_kv_heads][head_dim], bf16.
+ * scores [batch][n_q_heads][n_qblocks][n_qblocks] fp32 out; entries with
+ *   j > i or past a sequence's blocks are not written.
+ * n_qblocks >= ceil(max_seqlen / block_tokens), <= 4096 (layout of scores).
+ * Supported: bf16, head_dim 64 or 128, stride 4 or 8 with block = 16 * stride,
+ * G in {1, 2, 4, 8, 16}.  Fixed reduction orders: repeated calls are bitwise
+ * identical.
+ * Errors: NULL pointer, batch/max_seqlen <= 0, bad heads, sm_scale not finite
+ * or <= 0, block != 16 * stride, n_qblocks out of range -> FA_ERR_INVALID_ARG;
+ * other dtype / head_dim / stride / G -> FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_xattn_scores(const void *q, const void *k, int32_t dtype,
+                          const int32_t *cu_seqlens, int32_t batch,
+                          int32_t max_seqlen, int32_t n_q_heads,
+                          int32_t n_kv_heads, int32_t head_dim,
+                          int32_t block_tokens, int32_t stride, float sm_scale,
+                          float *scores, int32_t n_qblocks, void *stream);
+
+/*
+ * fa_xattn_select -- kept blocks per (sequence, head, query block i): block 0
+ * and block i always; then the blocks j < i in order of decreasing score
+ * (ties: smaller j first) join while the kept sum is below
+ * threshold * sum_{j<=i} scores[i][j].  The sums are fp32, the total in
+ * ascending j, the kept sum in the order blocks join, so the decision is a
+ * fixed function of the fp32 scores.
+ * mask [batch][n_q_heads][n_qblocks][ceil(n_qblocks / 32)] uint32 out: bit j
+ *   of row i set iff key block j is kept; rows past a sequence are zero.
+ * Errors: NULL pointer, batch/heads/block <= 0, n_qblocks outside [1, 4096],
+ * threshold not finite or <= 0 -> FA_ERR_INVALID_ARG.
+ */
+fa_status fa_xattn_select(const float *scores, const int32_t *cu_seqlens,
+                          int32_t batch, int32_t n_q_heads, int32_t n_qblocks,
+                          int32_t block_tokens, float threshold, uint32_t *mask,
+                          void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* Decode attention                                                         */
 /* ------------------------------------------------------------------------ */
 

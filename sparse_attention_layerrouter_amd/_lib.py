@@ -22,7 +22,8 @@ FA_F32, FA_BF16 = 0, 1
 EXPORTS = (
     "fa_last_error", "fa_abi_version", "fa_router_workspace_size", "fa_router_decide",
     "fa_block_plan", "fa_attn_prefill", "fa_decode_workspace_size", "fa_attn_decode",
-    "fa_kv_compact", "fa_attn_decode_ring", "fa_attn_prefill_kv",
+    "fa_kv_compact", "fa_attn_decode_ring", "fa_attn_prefill_kv", "fa_xattn_scores",
+    "fa_xattn_select",
 )
 
 
@@ -61,6 +62,10 @@ def lib() -> ctypes.CDLL:
     L.fa_attn_prefill_kv.restype = I32
     L.fa_attn_prefill_kv.argtypes = [P, P, P, P, P, I32, P, P, I32, I32, I32, I32, I32, P, P,
                                      I32, I32, I32, I32, I32, F, P]
+    L.fa_xattn_scores.restype = I32
+    L.fa_xattn_scores.argtypes = [P, P, I32, P, I32, I32, I32, I32, I32, I32, I32, F, P, I32, P]
+    L.fa_xattn_select.restype = I32
+    L.fa_xattn_select.argtypes = [P, P, I32, I32, I32, I32, F, P, P]
     L.fa_decode_workspace_size.restype = SZ
     L.fa_decode_workspace_size.argtypes = [I32, I32, I32, I32]
     L.fa_attn_decode.restype = I32
@@ -200,6 +205,27 @@ def fa_attn_prefill_kv(q, k, v, o, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, rou
         route.shape[1], layer, sink_tokens, window_tokens, block_tokens, float(sm_scale),
         _stream(stream)))
     del keep
+
+
+def fa_xattn_scores(q, k, cu_seqlens, max_seqlen, block_tokens, stride, sm_scale, scores,
+                    stream=None):
+    """XAttention antidiagonal block scores: scores [B, Hq, NQB, NQB] float32 out."""
+    _require_cuda(q, k, cu_seqlens, scores)
+    batch = cu_seqlens.numel() - 1
+    _, hq, d = q.shape
+    _check(lib().fa_xattn_scores(
+        _ptr(q), _ptr(k), _dtype_code(q), _ptr(cu_seqlens), batch, int(max_seqlen), hq,
+        k.shape[1], d, block_tokens, stride, float(sm_scale), _ptr(scores), scores.shape[2],
+        _stream(stream)))
+
+
+def fa_xattn_select(scores, cu_seqlens, block_tokens, threshold, mask, stream=None):
+    """XAttention block selection: mask [B, Hq, NQB, ceil(NQB/32)] int32 (uint32 bits) out."""
+    _require_cuda(scores, cu_seqlens, mask)
+    batch, hq, nqb = scores.shape[0], scores.shape[1], scores.shape[2]
+    _check(lib().fa_xattn_select(
+        _ptr(scores), _ptr(cu_seqlens), batch, hq, nqb, block_tokens, float(threshold),
+        _ptr(mask), _stream(stream)))
 
 
 def fa_attn_decode(q, o, k_cache, v_cache, cache_len, route, layer, sink_tokens, window_tokens,

@@ -31,11 +31,12 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
-SOURCES = ["router.hip", "prefill.hip", "decode.hip", "api.cpp"]
+SOURCES = ["router.hip", "prefill.hip", "decode.hip", "xattn.hip", "api.cpp"]
 # The hot MFMA / split-K kernels keep everything in registers: a build whose
 # compiler places any of their state in scratch memory (spills or a stack
 # array) is refused, since it would run many times slower.
-HOT_KERNELS = ("prefill_bf16_kernel", "decode_bf16_kernel", "decode_split_kernel")
+HOT_KERNELS = ("prefill_bf16_kernel", "decode_bf16_kernel", "decode_split_kernel",
+               "xa_score_kernel")
 _REMARK = re.compile(r"remark:\s+(Function Name|ScratchSize \[bytes/lane\]|VGPRs Spill|VGPRs|AGPRs"
                      r"|LDS Size \[bytes/block\]|Occupancy \[waves/SIMD\]):\s+(\S+)")
 

@@ -135,7 +135,7 @@ extern "C" {
 
 const char *fa_last_error(void) { return g_last_error.c_str(); }
 
-int32_t fa_abi_version(void) { return 4; }
+int32_t fa_abi_version(void) { return 5; }
 
 size_t fa_router_workspace_size(int32_t batch, int32_t hidden, int32_t router_hidden)
 {
@@ -238,6 +238,82 @@ fa_status fa_attn_prefill_kv(const void *q, const void *k, const void *v, void *
                         batch, max_seqlen_q, n_q_heads, n_kv_heads, head_dim, route, route_host,
                         n_layers, layer, sink_tokens, window_tokens, block_tokens, sm_scale,
                         stream);
+}
+
+fa_status fa_xattn_scores(const void *q, const void *k, int32_t dtype,
+                          const int32_t *cu_seqlens, int32_t batch, int32_t max_seqlen,
+                          int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                          int32_t block_tokens, int32_t stride, float sm_scale, float *scores,
+                          int32_t n_qblocks, void *stream)
+{
+    const char *fn = "fa_xattn_scores";
+    if (!q || !k || !cu_seqlens || !scores)
+        return fail(FA_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    if (batch <= 0 || max_seqlen <= 0)
+        return fail(FA_ERR_INVALID_ARG, "%s: batch=%d max_seqlen=%d must be positive", fn, batch,
+                    max_seqlen);
+    if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0)
+        return fail(FA_ERR_INVALID_ARG,
+                    "%s: n_q_heads=%d must be a positive multiple of n_kv_heads=%d", fn,
+                    n_q_heads, n_kv_heads);
+    if (!std::isfinite(sm_scale) || sm_scale <= 0.0f)
+        return fail(FA_ERR_INVALID_ARG, "%s: sm_scale must be finite and > 0", fn);
+    if (stride != 4 && stride != 8)
+        return fail(FA_ERR_UNSUPPORTED, "%s: stride %d not in {4, 8}", fn, stride);
+    if (block_tokens != 16 * stride)
+        return fail(FA_ERR_INVALID_ARG, "%s: block %d must be 16 * stride = %d", fn, block_tokens,
+                    16 * stride);
+    const int64_t need = ((int64_t)max_seqlen + block_tokens - 1) / block_tokens;
+    if (n_qblocks < need || n_qblocks > 4096)
+        return fail(FA_ERR_INVALID_ARG, "%s: n_qblocks %d must be in [%lld, 4096]", fn, n_qblocks,
+                    (long long)need);
+    if (dtype != FA_BF16)
+        return fail(FA_ERR_UNSUPPORTED, "%s: dtype %d is not FA_BF16", fn, dtype);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", fn, head_dim);
+    const int G = n_q_heads / n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+        return fail(FA_ERR_UNSUPPORTED, "%s: GQA ratio %d not in {1,2,4,8,16}", fn, G);
+    fa::XaScoreArgs a{};
+    a.q = q;
+    a.k = k;
+    a.cu_seqlens = cu_seqlens;
+    a.batch = batch;
+    a.hq = n_q_heads;
+    a.hkv = n_kv_heads;
+    a.d = head_dim;
+    a.stride = stride;
+    a.nqb = n_qblocks;
+    a.sm_scale = sm_scale;
+    a.scores = scores;
+    return hip_status(fa::launch_xa_scores(a, (hipStream_t)stream), fn);
+}
+
+fa_status fa_xattn_select(const float *scores, const int32_t *cu_seqlens, int32_t batch,
+                          int32_t n_q_heads, int32_t n_qblocks, int32_t block_tokens,
+                          float threshold, uint32_t *mask, void *stream)
+{
+    const char *fn = "fa_xattn_select";
+    if (!scores || !cu_seqlens || !mask)
+        return fail(FA_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    if (batch <= 0 || n_q_heads <= 0 || block_tokens <= 0)
+        return fail(FA_ERR_INVALID_ARG, "%s: batch=%d heads=%d block=%d must be positive", fn,
+                    batch, n_q_heads, block_tokens);
+    if (n_qblocks <= 0 || n_qblocks > 4096)
+        return fail(FA_ERR_INVALID_ARG, "%s: n_qblocks %d not in [1, 4096]", fn, n_qblocks);
+    if (!std::isfinite(threshold) || threshold <= 0.0f)
+        return fail(FA_ERR_INVALID_ARG, "%s: threshold must be finite and > 0", fn);
+    fa::XaSelectArgs a{};
+    a.scores = scores;
+    a.cu_seqlens = cu_seqlens;
+    a.batch = batch;
+    a.hq = n_q_heads;
+    a.nqb = n_qblocks;
+    a.nw = (n_qblocks + 31) / 32;
+    a.block = block_tokens;
+    a.threshold = threshold;
+    a.mask = mask;
+    return hip_status(fa::launch_xa_select(a, (hipStream_t)stream), fn);
 }
 
 size_t fa_decode_workspace_size(int32_t batch, int32_t n_q_heads, int32_t head_dim,

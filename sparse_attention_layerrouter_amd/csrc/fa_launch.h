@@ -92,6 +92,27 @@ struct CompactArgs {
 };
 hipError_t launch_kv_compact(const CompactArgs &a, hipStream_t stream);
 
+// XAttention branch: antidiagonal block scores and threshold selection
+struct XaScoreArgs {
+    const void *q, *k;              // bf16 [total][hq][d], [total][hkv][d]
+    const int32_t *cu_seqlens;
+    int batch, hq, hkv, d;
+    int stride;                     // S; block = 16 S
+    int nqb;                        // query blocks per sequence in the score layout
+    float sm_scale;
+    float *scores;                  // [batch][hq][nqb][nqb]
+};
+hipError_t launch_xa_scores(const XaScoreArgs &a, hipStream_t stream);
+
+struct XaSelectArgs {
+    const float *scores;
+    const int32_t *cu_seqlens;
+    int batch, hq, nqb, nw, block;
+    float threshold;
+    uint32_t *mask;                 // [batch][hq][nqb][nw] kept-block bits
+};
+hipError_t launch_xa_select(const XaSelectArgs &a, hipStream_t stream);
+
 // Split policy shared by fa_decode_workspace_size and fa_attn_decode.
 int decode_split_tokens(int max_kept_tokens);
 inline int decode_n_splits(int max_kept_tokens)
