@@ -258,6 +258,30 @@ fa_status fa_xattn_select(const float *scores, const int32_t *cu_seqlens,
                           int32_t block_tokens, float threshold, uint32_t *mask,
                           void *stream);
 
+/*
+ * fa_attn_prefill_xattn -- prefill attention of one layer over kept blocks:
+ * query t of head h sees key s iff s <= t and key block s / block is kept for
+ * query block t / block of head h in mask (the output of fa_xattn_select, or
+ * any mask of that layout).  Within a kept block the rule is token-causal;
+ * a block is never loaded unless some head of the workgroup keeps it.
+ * q, k, v, o, lse, cu_seqlens, batch, max_seqlen, heads, head_dim as
+ * fa_attn_prefill; mask [batch][n_q_heads][n_qblocks][ceil(n_qblocks / 32)]
+ * uint32 device, bit j of row i = key block j kept for query block i.
+ * Supported: bf16 (MFMA kernel when 256 / min(G, 4) <= block, else the plain
+ * kernel) and fp32, head_dim 64 or 128, block 64 or 128.
+ * Errors: NULL pointer, batch/max_seqlen <= 0, bad heads, sm_scale not finite
+ * or <= 0, block not in {64, 128}, n_qblocks outside
+ * [ceil(max_seqlen / block), 4096] -> FA_ERR_INVALID_ARG; other dtype /
+ * head_dim -> FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_attn_prefill_xattn(const void *q, const void *k, const void *v, void *o,
+                                float *lse, int32_t dtype,
+                                const int32_t *cu_seqlens, int32_t batch,
+                                int32_t max_seqlen, int32_t n_q_heads,
+                                int32_t n_kv_heads, int32_t head_dim,
+                                int32_t block_tokens, const uint32_t *mask,
+                                int32_t n_qblocks, float sm_scale, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Decode attention                                                         */
 /* ------------------------------------------------------------------------ */

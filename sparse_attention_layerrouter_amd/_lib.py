@@ -23,7 +23,7 @@ EXPORTS = (
     "fa_last_error", "fa_abi_version", "fa_router_workspace_size", "fa_router_decide",
     "fa_block_plan", "fa_attn_prefill", "fa_decode_workspace_size", "fa_attn_decode",
     "fa_kv_compact", "fa_attn_decode_ring", "fa_attn_prefill_kv", "fa_xattn_scores",
-    "fa_xattn_select",
+    "fa_xattn_select", "fa_attn_prefill_xattn",
 )
 
 
@@ -66,6 +66,9 @@ def lib() -> ctypes.CDLL:
     L.fa_xattn_scores.argtypes = [P, P, I32, P, I32, I32, I32, I32, I32, I32, I32, F, P, I32, P]
     L.fa_xattn_select.restype = I32
     L.fa_xattn_select.argtypes = [P, P, I32, I32, I32, I32, F, P, P]
+    L.fa_attn_prefill_xattn.restype = I32
+    L.fa_attn_prefill_xattn.argtypes = [P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, I32, P,
+                                        I32, F, P]
     L.fa_decode_workspace_size.restype = SZ
     L.fa_decode_workspace_size.argtypes = [I32, I32, I32, I32]
     L.fa_attn_decode.restype = I32
@@ -226,6 +229,18 @@ def fa_xattn_select(scores, cu_seqlens, block_tokens, threshold, mask, stream=No
     _check(lib().fa_xattn_select(
         _ptr(scores), _ptr(cu_seqlens), batch, hq, nqb, block_tokens, float(threshold),
         _ptr(mask), _stream(stream)))
+
+
+def fa_attn_prefill_xattn(q, k, v, o, cu_seqlens, max_seqlen, block_tokens, mask, sm_scale,
+                          lse=None, stream=None):
+    """Prefill over kept blocks: mask [B, Hq, NQB, ceil(NQB/32)] (uint32 bits as int32)."""
+    _require_cuda(q, k, v, o, cu_seqlens, mask, lse)
+    batch = cu_seqlens.numel() - 1
+    _, hq, d = q.shape
+    _check(lib().fa_attn_prefill_xattn(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dtype_code(q), _ptr(cu_seqlens), batch,
+        int(max_seqlen), hq, k.shape[1], d, block_tokens, _ptr(mask), mask.shape[2],
+        float(sm_scale), _stream(stream)))
 
 
 def fa_attn_decode(q, o, k_cache, v_cache, cache_len, route, layer, sink_tokens, window_tokens,

@@ -316,6 +316,63 @@ fa_status fa_xattn_select(const float *scores, const int32_t *cu_seqlens, int32_
     return hip_status(fa::launch_xa_select(a, (hipStream_t)stream), fn);
 }
 
+fa_status fa_attn_prefill_xattn(const void *q, const void *k, const void *v, void *o,
+                                float *lse, int32_t dtype, const int32_t *cu_seqlens,
+                                int32_t batch, int32_t max_seqlen, int32_t n_q_heads,
+                                int32_t n_kv_heads, int32_t head_dim, int32_t block_tokens,
+                                const uint32_t *mask, int32_t n_qblocks, float sm_scale,
+                                void *stream)
+{
+    const char *fn = "fa_attn_prefill_xattn";
+    if (!q || !k || !v || !o || !cu_seqlens || !mask)
+        return fail(FA_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    if (batch <= 0 || max_seqlen <= 0)
+        return fail(FA_ERR_INVALID_ARG, "%s: batch=%d max_seqlen=%d must be positive", fn, batch,
+                    max_seqlen);
+    if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0)
+        return fail(FA_ERR_INVALID_ARG,
+                    "%s: n_q_heads=%d must be a positive multiple of n_kv_heads=%d", fn,
+                    n_q_heads, n_kv_heads);
+    if (!std::isfinite(sm_scale) || sm_scale <= 0.0f)
+        return fail(FA_ERR_INVALID_ARG, "%s: sm_scale must be finite and > 0", fn);
+    if (block_tokens != 64 && block_tokens != 128)
+        return fail(FA_ERR_INVALID_ARG, "%s: block %d not in {64, 128}", fn, block_tokens);
+    const int64_t need = ((int64_t)max_seqlen + block_tokens - 1) / block_tokens;
+    if (n_qblocks < need || n_qblocks > 4096)
+        return fail(FA_ERR_INVALID_ARG, "%s: n_qblocks %d must be in [%lld, 4096]", fn, n_qblocks,
+                    (long long)need);
+    if (dtype != FA_F32 && dtype != FA_BF16)
+        return fail(FA_ERR_UNSUPPORTED, "%s: dtype %d is not FA_F32/FA_BF16", fn, dtype);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", fn, head_dim);
+    fa::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.bf16 = dtype == FA_BF16;
+    a.cu_seqlens = cu_seqlens;
+    a.cu_seqlens_k = cu_seqlens;
+    a.batch = batch;
+    a.max_seqlen = max_seqlen;
+    a.hq = n_q_heads;
+    a.hkv = n_kv_heads;
+    a.d = head_dim;
+    a.route = nullptr;
+    a.n_layers = 1;
+    a.layer = 0;
+    a.ns = 0;
+    a.nw = 1;
+    a.bk_log2 = block_tokens == 64 ? 6 : 7;
+    a.sm_scale = sm_scale;
+    a.mode = fa::kModeXA;
+    a.xa_mask = mask;
+    a.xa_nqb = n_qblocks;
+    a.xa_nw = (n_qblocks + 31) / 32;
+    return hip_status(fa::launch_prefill(a, (hipStream_t)stream), fn);
+}
+
 size_t fa_decode_workspace_size(int32_t batch, int32_t n_q_heads, int32_t head_dim,
                                 int32_t max_cache)
 {

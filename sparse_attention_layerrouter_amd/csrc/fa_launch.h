@@ -15,6 +15,7 @@ namespace fa {
 constexpr int kModeMixed = 0;  // read each sequence's bit from the device mask
 constexpr int kModeFA = 1;     // every sequence is FA for this layer
 constexpr int kModeSA = 2;     // every sequence is SA for this layer
+constexpr int kModeXA = 3;     // prefill over kept-block masks (XAttention branch)
 
 struct RouterArgs {
     const void *x_q;
@@ -54,7 +55,10 @@ struct PrefillArgs {
     int n_layers, layer;
     int ns, nw, bk_log2;
     float sm_scale;
-    int mode;  // kModeMixed / kModeFA / kModeSA
+    int mode;  // kModeMixed / kModeFA / kModeSA / kModeXA
+    // kModeXA: kept-block bits [batch][hq][xa_nqb][xa_nw]; the block size is 1 << bk_log2
+    const uint32_t *xa_mask;
+    int xa_nqb, xa_nw;
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 

@@ -148,9 +148,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int32_t *__restrict__ cu, const int32_t *__restrict__ cu_k,
     const uint8_t *__restrict__ route, int n_layers, int layer,
     int hq, int hkv, int G, int hpw, int n_hgroups, int n_units, int n_ptiles,
-    SparseRule rule, float scale_log2)
+    SparseRule rule, float scale_log2, const uint32_t *__restrict__ xa_mask, int xa_nqb,
+    int xa_nw)
 {
     constexpr int TILE_BYTES = kBN * D * 2;
+    constexpr bool XA = MODE == kModeXA;
+    // XA: kept-block words of the workgroup's heads, their union as a block list
+    __shared__ uint32_t xa_head[XA ? 4 : 1][XA ? 128 : 1];
+    __shared__ uint16_t xa_list[XA ? 4096 : 1];
+    __shared__ int xa_pre[XA ? 129 : 1];
     // separate arrays per buffer: the compiler can then tell that reads of one
     // buffer never wait for the asynchronous copies into the other
     __shared__ __attribute__((aligned(1024))) char k_lds0[TILE_BYTES];
@@ -202,7 +208,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     }
     const int p0 = q_off + r0;      // positions of this workgroup: p0 .. p1-1
     const int p1 = min(p0 + 2 * gpos, T);
-    const bool is_fa = MODE == kModeFA ? true
+    const bool is_fa = MODE == kModeFA || MODE == kModeXA ? true
                        : MODE == kModeSA ? false
                                          : route[(size_t)b * n_layers + layer] != 0;
 
@@ -210,15 +216,58 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const bool wave_active = pw0 < T;
     const int pw_last = min(pw0 + 31, T - 1);  // last valid position of the wave
 
-    // ---- KV tile schedule: [0, nA) then [tB0, tB0 + nB)
-    int a_end, b_begin;
-    kept_ranges(p0, p1, is_fa, rule, a_end, b_begin);
-    const int nA = (a_end + kBN - 1) / kBN;
-    const int tB0 = max(nA, b_begin / kBN);
-    const int tB1 = (p1 + kBN - 1) / kBN;
-    const int nB = max(0, tB1 - tB0);
-    const int n_tiles = nA + nB;
-    auto tile_k0 = [&](int t) __attribute__((always_inline)) { return (t < nA ? t : tB0 + (t - nA)) * kBN; };
+    // ---- KV tile schedule: [0, nA) then [tB0, tB0 + nB); in mode XA the kept
+    // blocks of the workgroup's query block (all its positions lie in one block),
+    // the union over its heads in ascending order, each block kBN-tiled.
+    int nA = 0, tB0 = 0, n_tiles = 0;
+    if constexpr (XA) {
+        const int qi = p0 >> rule.bk_log2;
+        const size_t hstep = (size_t)xa_nqb * xa_nw;
+        const uint32_t *mrow =
+            xa_mask + (((size_t)b * hq + kvh * G + hg * hpw) * xa_nqb + qi) * xa_nw;
+        for (int w = tid; w < xa_nw; w += kThreads) {
+            uint32_t u = 0;
+            for (int hh = 0; hh < hpw; ++hh) {
+                const uint32_t x = mrow[hh * hstep + w];
+                xa_head[hh][w] = x;
+                u |= x;
+            }
+            xa_pre[w + 1] = __builtin_popcount(u);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            xa_pre[0] = 0;
+            for (int w = 0; w < xa_nw; ++w) xa_pre[w + 1] += xa_pre[w];
+        }
+        __syncthreads();
+        for (int w = tid; w < xa_nw; w += kThreads) {
+            uint32_t u = 0;
+            for (int hh = 0; hh < hpw; ++hh) u |= xa_head[hh][w];
+            int o = xa_pre[w];
+            while (u) {
+                xa_list[o++] = (uint16_t)(32 * w + __builtin_ctz(u));
+                u &= u - 1;
+            }
+        }
+        __syncthreads();
+        n_tiles = __builtin_amdgcn_readfirstlane(xa_pre[xa_nw]) << (rule.bk_log2 - 6);
+    } else {
+        int a_end, b_begin;
+        kept_ranges(p0, p1, is_fa, rule, a_end, b_begin);
+        nA = (a_end + kBN - 1) / kBN;
+        tB0 = max(nA, b_begin / kBN);
+        const int tB1 = (p1 + kBN - 1) / kBN;
+        n_tiles = nA + max(0, tB1 - tB0);
+    }
+    auto tile_k0 = [&](int t) __attribute__((always_inline)) {
+        if constexpr (XA) {
+            const int sh = rule.bk_log2 - 6;  // kBN = 64 keys per tile
+            const int blk = __builtin_amdgcn_readfirstlane((int)xa_list[t >> sh]);
+            return (blk << rule.bk_log2) + ((t & ((1 << sh) - 1)) << 6);
+        } else {
+            return (t < nA ? t : tB0 + (t - nA)) * kBN;
+        }
+    };
 
     const size_t row_stride = (size_t)hkv * D;
     const uint16_t *kb = k + ((size_t)start * hkv + kvh) * D;
@@ -261,8 +310,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int my_win_lo = ((my_t >> rule.bk_log2) - rule.nw + 1) << rule.bk_log2;
     // does any row of this wave see a key of the tile at k0?
     auto wave_sees = [&](int k0) __attribute__((always_inline)) {
-        return wave_active && k0 <= pw_last &&
-               (is_fa || k0 < sink_tok || k0 + kBN > win_lo_min);
+        if constexpr (XA) {  // this wave's head kept the tile's block
+            const int blk = k0 >> rule.bk_log2;
+            return wave_active && k0 <= pw_last &&
+                   ((xa_head[wq / wph][blk >> 5] >> (blk & 31)) & 1u) != 0;
+        } else {
+            return wave_active && k0 <= pw_last &&
+                   (is_fa || k0 < sink_tok || k0 + kBN > win_lo_min);
+        }
     };
 
     // Per-lane LDS byte offsets, fixed for the whole kernel (the 32-key block
@@ -552,7 +607,8 @@ __global__ __launch_bounds__(64) void prefill_generic_kernel(
     const TE *__restrict__ q, const TE *__restrict__ k, const TE *__restrict__ v,
     TE *__restrict__ o, float *__restrict__ lse, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ cu_k, const uint8_t *__restrict__ route, int n_layers,
-    int layer, int hq, int hkv, SparseRule rule, float scale_log2)
+    int layer, int hq, int hkv, SparseRule rule, float scale_log2,
+    const uint32_t *__restrict__ xa_mask, int xa_nqb, int xa_nw)
 {
     const int b = blockIdx.z;
     const int h = blockIdx.y;
@@ -579,11 +635,15 @@ __global__ __launch_bounds__(64) void prefill_generic_kernel(
     const int p0 = q_off + r0;
     const int p1 = min(p0 + 64, T);
     const int t = min(p0 + (int)threadIdx.x, T - 1);
-    const bool is_fa = MODE == kModeFA ? true
+    const bool is_fa = MODE == kModeFA || MODE == kModeXA ? true
                        : MODE == kModeSA ? false
                                          : route[(size_t)b * n_layers + layer] != 0;
     const int G = hq / hkv;
     const int g = h / G;
+    // XA: this row's kept-block words (query block t / B of head h)
+    const uint32_t *xrow =
+        MODE == kModeXA ? xa_mask + (((size_t)b * hq + h) * xa_nqb + (t >> rule.bk_log2)) * xa_nw
+                        : nullptr;
 
     float qv[D], acc[D];
     const TE *qr = q + ((size_t)(start_q + t - q_off) * hq + h) * D;
@@ -600,6 +660,10 @@ __global__ __launch_bounds__(64) void prefill_generic_kernel(
         int s1 = pass == 0 ? a_end : p1;
         for (int s = s0; s < s1; ++s) {
             if (!visible(t, s, is_fa, rule)) continue;
+            if constexpr (MODE == kModeXA) {
+                const int blk = s >> rule.bk_log2;
+                if (((xrow[blk >> 5] >> (blk & 31)) & 1u) == 0) continue;
+            }
             const TE *kr = k + ((size_t)(start + s) * hkv + g) * D;
             const TE *vr = v + ((size_t)(start + s) * hkv + g) * D;
             float dot = 0.0f;
@@ -635,7 +699,8 @@ hipError_t launch_generic(const PrefillArgs &a, hipStream_t stream, const Sparse
     dim3 grid((a.max_seqlen + 63) / 64, a.hq, a.batch);
     prefill_generic_kernel<TE, D, MODE><<<grid, 64, 0, stream>>>(
         (const TE *)a.q, (const TE *)a.k, (const TE *)a.v, (TE *)a.o, a.lse, a.cu_seqlens,
-        a.cu_seqlens_k, a.route, a.n_layers, a.layer, a.hq, a.hkv, r, scale_log2);
+        a.cu_seqlens_k, a.route, a.n_layers, a.layer, a.hq, a.hkv, r, scale_log2, a.xa_mask,
+        a.xa_nqb, a.xa_nw);
     return hipGetLastError();
 }
 
@@ -654,7 +719,7 @@ hipError_t launch_mfma(const PrefillArgs &a, hipStream_t stream, const SparseRul
     prefill_bf16_kernel<D, MODE><<<(unsigned)n_wg, kThreads, 0, stream>>>(
         (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, (uint16_t *)a.o,
         a.lse, a.cu_seqlens, a.cu_seqlens_k, a.route, a.n_layers, a.layer, a.hq, a.hkv, G, hpw,
-        n_hgroups, n_units, n_ptiles, r, scale_log2);
+        n_hgroups, n_units, n_ptiles, r, scale_log2, a.xa_mask, a.xa_nqb, a.xa_nw);
     return hipGetLastError();
 }
 
@@ -668,7 +733,10 @@ hipError_t launch_mode(const PrefillArgs &a, hipStream_t stream, const SparseRul
                        float scale_log2)
 {
     const int G = a.hq / a.hkv;
-    if (a.bf16 && prefill_mfma_supported(a.d, G)) {
+    // mode XA needs every workgroup's positions (2 groups x 32 x 4 / min(G, 4))
+    // inside one block
+    const bool xa_fits = MODE != kModeXA || 256 / (G >= 4 ? 4 : G) <= (1 << a.bk_log2);
+    if (a.bf16 && prefill_mfma_supported(a.d, G) && xa_fits) {
         if (a.d == 128) return launch_mfma<128, MODE>(a, stream, r, scale_log2);
         return launch_mfma<64, MODE>(a, stream, r, scale_log2);
     }
@@ -689,6 +757,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream)
     switch (a.mode) {
     case kModeFA: return launch_mode<kModeFA>(a, stream, r, scale_log2);
     case kModeSA: return launch_mode<kModeSA>(a, stream, r, scale_log2);
+    case kModeXA: return launch_mode<kModeXA>(a, stream, r, scale_log2);
     default: return launch_mode<kModeMixed>(a, stream, r, scale_log2);
     }
 }

@@ -27,7 +27,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert set(names) == set(_lib.EXPORTS)
     for name in names:
         assert hasattr(L, name), name

@@ -88,3 +88,92 @@ def test_scores_are_deterministic():
     a = run_scores(q, k, cu, 128, 8, 0.088, 16)
     b = run_scores(q, k, cu, 128, 8, 0.088, 16)
     assert torch.equal(a, b)
+
+
+def pack(keep):
+    """bool [B, H, NQB, NQB] -> int32 words [B, H, NQB, ceil(NQB/32)]."""
+    B, H, n, _ = keep.shape
+    nw = -(-n // 32)
+    pad = np.zeros((B, H, n, nw * 32), bool)
+    pad[..., :n] = keep
+    w = (pad.reshape(B, H, n, nw, 32).astype(np.uint64) << np.arange(32, dtype=np.uint64)).sum(-1)
+    return w.astype(np.uint32).view(np.int32)
+
+
+def run_xattn_prefill(q, k, v, cu, block, keep_words, scale):
+    qd = dev_from(q)
+    o = torch.empty_like(qd)
+    lse = torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=DEV)
+    _lib.fa_attn_prefill_xattn(qd, dev_from(k), dev_from(v), o, torch.tensor(cu, device=DEV),
+                               int(np.diff(cu).max()), block, torch.tensor(keep_words, device=DEV),
+                               scale, lse=lse)
+    torch.cuda.synchronize()
+    t = o.contiguous()
+    host = t.view(torch.int16).cpu().numpy().view(np.uint16) if t.dtype == torch.bfloat16 \
+        else t.cpu().numpy()
+    return host, lse.cpu().numpy()
+
+
+def as_f64(a):
+    return (synth.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a).astype(np.float64)
+
+
+XA_CASES = [
+    # lengths, hq, hkv, d, block, bf16, mask kind
+    ([1000, 333, 64, 1], 8, 2, 128, 128, True, "selected"),
+    ([700, 130], 8, 2, 128, 64, True, "random"),
+    ([517], 4, 4, 128, 128, True, "random"),        # G = 1: plain kernel
+    ([390, 200], 16, 2, 64, 128, True, "random"),   # G = 8, d = 64
+    ([300, 90], 8, 2, 128, 64, False, "random"),    # fp32: plain kernel
+    ([600], 4, 2, 128, 128, True, "random"),        # G = 2, block 128: MFMA kernel
+]
+
+
+@pytest.mark.parametrize("case", XA_CASES)
+def test_xattn_prefill_matches_oracle(case):
+    lengths, hq, hkv, d, block, bf16, kind = case
+    rng = np.random.default_rng(sum(lengths) + hq + block)
+    cu = synth.cu_seqlens_of(lengths)
+    q, k, v = synth.qkv_host(rng, int(cu[-1]), hq, hkv, d, bf16=bf16)
+    scale = 1 / math.sqrt(d)
+    nqb = -(-max(lengths) // block)
+    if kind == "selected":
+        sc = run_scores(q, k, cu, block, block // 16, scale, nqb)
+        nw = -(-nqb // 32)
+        m = torch.zeros((len(lengths), hq, nqb, nw), dtype=torch.int32, device=DEV)
+        _lib.fa_xattn_select(sc, torch.tensor(cu, device=DEV), block, 0.9, m)
+        torch.cuda.synchronize()
+        words = m.cpu().numpy()
+        keep = unpack(words, nqb)
+    else:
+        keep = rng.random((len(lengths), hq, nqb, nqb)) < 0.45
+        idx = np.arange(nqb)
+        keep[..., idx, idx] = True                   # every row keeps its own block
+        keep &= np.tril(np.ones((nqb, nqb), bool))   # causal blocks only
+        words = pack(keep)
+    o, lse = run_xattn_prefill(q, k, v, cu, block, words, scale)
+    o_ref, l_ref = xattn.attn_prefill(q, k, v, cu, keep, block, scale)
+    tol, tol_lse = (2e-2, 1e-3) if bf16 else (1e-4, 1e-4)
+    assert np.abs(as_f64(o) - o_ref).max() <= tol
+    assert np.abs(lse - l_ref).max() <= tol_lse
+
+
+@pytest.mark.parametrize("block", [64, 128])
+def test_xattn_prefill_with_every_block_kept_is_the_fa_kernel(block):
+    rng = np.random.default_rng(12)
+    lengths, hq, hkv, d = [1000, 257], 8, 2, 128
+    cu = synth.cu_seqlens_of(lengths)
+    q, k, v = synth.qkv_host(rng, int(cu[-1]), hq, hkv, d, bf16=True)
+    nqb = -(-max(lengths) // block)
+    keep = np.broadcast_to(np.tril(np.ones((nqb, nqb), bool)), (2, hq, nqb, nqb)).copy()
+    o, lse = run_xattn_prefill(q, k, v, cu, block, pack(keep), 0.09)
+    qd, kd, vd = dev_from(q), dev_from(k), dev_from(v)
+    o_fa = torch.empty_like(qd)
+    l_fa = torch.empty((q.shape[0], hq), dtype=torch.float32, device=DEV)
+    route = np.ones((2, 1), np.uint8)
+    _lib.fa_attn_prefill(qd, kd, vd, o_fa, torch.tensor(cu, device=DEV), max(lengths),
+                         torch.tensor(route, device=DEV), 0, 0, 64, 64, 0.09, lse=l_fa,
+                         route_host=route)
+    torch.cuda.synchronize()
+    assert np.array_equal(o, o_fa.view(torch.int16).cpu().numpy().view(np.uint16))
+    assert np.array_equal(lse, l_fa.cpu().numpy())
