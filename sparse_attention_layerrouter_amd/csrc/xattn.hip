@@ -16,21 +16,28 @@
 //   (ties: smaller j) while the kept sum is below tau * sum_j score[i][j], with
 //   every sum in fp32 in that order.
 //
-// Score kernel: one workgroup per (query block, 4 query heads of one KV head).
-// Each wave keeps its head's 16 reshaped query rows in registers as the B
+// Score kernel: one workgroup of 8 waves per (pair of query blocks 2m, 2m+1,
+// 4 query heads of one KV head); wave w handles query block 2m + w/4 and head
+// w%4.  Each wave keeps its head's 16 reshaped query rows in registers as the B
 // operand of v_mfma_f32_16x16x32_bf16 (S*d / 32 k-steps); the key block --
-// whose B rows are exactly the 16 reshaped key columns, S rows each -- is staged
-// in LDS once for the 4 heads and read as the A operand.  Two passes over the
-// key blocks: the first finds every reshaped row's log-sum-exp, the second
-// sums 2^(A - lse) per key block.  No workspace; fixed reduction orders.
+// whose B rows are exactly the 16 reshaped key columns, S rows each -- is copied
+// straight from global memory into LDS (buffer loads with an LDS destination,
+// three buffers, two tiles ahead) once for all 8 waves and read as the A
+// operand, 8 reads in flight ahead of the matrix core.  Two passes over the key
+// blocks: the first finds every reshaped row's log-sum-exp, the second sums
+// 2^(A - lse) per key block.  No workspace; fixed reduction orders.
 #include "fa_common.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
 
+typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kXaRows = 16;  // reshaped rows (and columns) per block: B = 16 S
 constexpr int kXaMaxBlocks = 4096;
+constexpr int kXaRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kXaLook = 8;                // LDS operand reads in flight
+constexpr int kXaWaves = 8;
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c)
 {
@@ -49,38 +56,131 @@ __device__ __forceinline__ float row4_max(float x)
     return max_xor32(x);
 }
 
+template <int V>
+using ic = std::integral_constant<int, V>;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// One 1 KiB copy from global memory into LDS: lane l moves the 16 bytes at
+// byte offset voff of the buffer described by rsrc to LDS address lds + 16 l
+// (a buffer load with an LDS destination, whose base sits in m0; reads past
+// the buffer's range return zeros).  Written as inline assembly so the
+// compiler places no waits for it: the kernel waits for its copies itself,
+// with explicit vmcnt waits.  m0 has no other user in these kernels; the copy
+// reads m0 one wait state after it is written (s_nop 0), as the hardware needs.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy_1k(uint32_t lds, uint32_t voff, i32x4 rsrc)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// raw buffer descriptor: base address, stride 0, num_records bytes
+__device__ __forceinline__ i32x4 raw_rsrc(const void *base, int num_records)
+{
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r.x = (int)(uint32_t)a;
+    r.y = (int)((uint32_t)(a >> 32) & 0xffffu);
+    r.z = num_records;
+    r.w = kXaRsrcWord3;
+    return r;
+}
+
+// s_waitcnt vmcnt(N) then s_barrier, through the builtins so the compiler's
+// own wait placement knows which copies are done; the empty asm statements keep
+// memory accesses from moving across.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier(ic<N>)
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 encoding: vmcnt[3:0] at bits 3:0, vmcnt[5:4] at bits 15:14; expcnt
+    // (bits 6:4) and lgkmcnt (bits 11:8) at their no-wait maxima
+    constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(imm);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 template <int D, int S>
-__global__ __launch_bounds__(256) void xa_score_kernel(
+__global__ __launch_bounds__(kXaWaves * 64) void xa_score_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const int32_t *__restrict__ cu,
-    int hq, int hkv, int G, int hpw, int n_hgroups, int n_units, int nqb, float scale_log2,
-    float *__restrict__ scores)
+    int hq, int hkv, int G, int hpw, int n_hgroups, int n_units, int npairs, int nqb,
+    float scale_log2, float *__restrict__ scores)
 {
     constexpr int B = kXaRows * S;   // positions per block
     constexpr int NK = S * D / 32;   // k-steps of one reshaped row
     constexpr int CH = D / 8;        // 16-byte chunks per key row
     constexpr int TILE = B * D * 2;  // bytes of one key block
-    constexpr int NCH = B * CH / 256;
-    static_assert(NCH * 256 == B * CH, "tile split over 256 threads");
-    __shared__ __attribute__((aligned(1024))) char lds[2][TILE];
+    constexpr int NI = TILE / (1024 * kXaWaves);  // 1 KiB copies per wave per tile
+    constexpr int NQ = D / 32;       // k-steps per key row
+    constexpr int LK = NK > 2 * kXaLook ? kXaLook : NK / 2;  // reads in flight
+    static_assert(NI >= 1 && NI * 1024 * kXaWaves == TILE, "tile split over the waves");
+    __shared__ __attribute__((aligned(1024))) char lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) char lds1[TILE];
+    __shared__ __attribute__((aligned(1024))) char lds2[TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, wq = wave & 3;
     int bid = blockIdx.x;
     const int unit = bid % n_units;
     bid /= n_units;
     const int hg = bid % n_hgroups;
-    const int i = nqb - 1 - bid / n_hgroups;  // query block; the heavy ones start first
+    const int pm = npairs - 1 - bid / n_hgroups;  // block pair; the heavy ones start first
     const int b = unit / hkv, kvh = unit % hkv;
     const int start = cu[b];
     const int T = cu[b + 1] - start;
     const int nb = (T + B - 1) / B;
-    if (i >= nb) return;                      // uniform
+    if (2 * pm >= nb) return;                 // uniform
+    const int i = 2 * pm + grp;               // this wave's query block
+    const int j_last = min(2 * pm + 1, nb - 1);  // last key block of the workgroup
     const int Tr = (T + S - 1) / S;           // reshaped rows of the sequence
-    const bool active = wave < hpw;
-    const int h = kvh * G + hg * hpw + (active ? wave : 0);
+    const bool active = wq < hpw && i < nb;
+    const int h = kvh * G + hg * hpw + (wq < hpw ? wq : 0);
     const size_t row_stride = (size_t)hkv * D;
     const uint16_t *kb = k + ((size_t)start * hkv + kvh) * D;
+
+    // Key block copies: LDS chunk p (16 bytes) of a tile holds key row r = p / CH,
+    // logical chunk (p % CH) ^ ((r / S) mod CH), so that the 16 lanes of one
+    // A-operand read (16 reshaped columns, key rows S apart) hit distinct banks.
+    // Wave w copies LDS chunks (w NI + n) 64 + lane, n < NI.
+    uint32_t goff[NI];
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+        const int p = (wave * NI + n) * 64 + lane;
+        const int r = p / CH;
+        const int c = (p % CH) ^ ((r / S) & (CH - 1));
+        goff[n] = (uint32_t)(r * row_stride * 2) + (uint32_t)(c << 4);
+    }
+    // Rows at or past the sequence end read as zero (buffer range check); a
+    // tile past the workgroup's last key block is issued with an empty range, so
+    // the copies are unconditional and every wave has NI of them per tile.
+    auto issue_tile = [&](int jt, char *dst) __attribute__((always_inline)) {
+        const long long bytes =
+            jt <= j_last ? (long long)(T - jt * B) * (long long)row_stride * 2 : 0LL;
+        const i32x4 rs =
+            raw_rsrc(kb + (size_t)jt * B * row_stride, (int)min(bytes, 0x7fffffffLL));
+        const uint32_t lds = (uint32_t)(uintptr_t)(lds_void *)dst + wave * NI * 1024;
+#pragma unroll
+        for (int n = 0; n < NI; ++n) lds_copy_1k(lds + n * 1024, goff[n], rs);
+    };
+    // Tile jt ready: this wave's copies of it are done (the NI copies of the next
+    // tile, issued later, may still run; memory operations complete in order),
+    // then every wave's.  The last block of a sequence may end inside the tile:
+    // its rows past the end are cleared so they never hold an earlier tile's keys.
+    auto tile_ready = [&](int jt, char *dst) __attribute__((always_inline)) {
+        vm_wait_barrier(ic<NI>{});
+        const int rows = T - jt * B;
+        if (jt <= j_last && rows < B) {  // uniform
+            for (int p = tid; p < TILE / 16; p += kXaWaves * 64)
+                if (p / CH >= rows) *(u32x4 *)(dst + 16 * p) = u32x4{0u, 0u, 0u, 0u};
+            __syncthreads();
+        }
+    };
 
     // B operand: lane l holds reshaped query row a = 16 i + l%16 at reshaped
     // k index kk*32 + 8*(l/16) .. +7, i.e. position a S + S-1-s, elements e .. e+7
@@ -97,89 +197,111 @@ __global__ __launch_bounds__(256) void xa_score_kernel(
         if (active && pos < T) w = *(const u32x4 *)(q + ((size_t)(start + pos) * hq + h) * D + e);
         qr[kk] = __builtin_bit_cast(bf16x8, w);
     }
+    // consume the query loads here, before any tile copy is in flight, so the
+    // waits the compiler places for them never cover a copy
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) asm volatile("" ::"v"(qr[kk]));
 
-    // Key block j into LDS: chunk p = tid + 256 n is row r = p / CH, chunk c = p % CH
-    // of the block, stored at chunk c ^ ((r / S) mod CH) so the 16 lanes of an
-    // A-operand read (16 reshaped columns, rows S apart) hit distinct banks.
-    u32x4 stage[NCH];
-    auto load_tile = [&](int j) __attribute__((always_inline)) {
-#pragma unroll
-        for (int n = 0; n < NCH; ++n) {
-            const int p = tid + 256 * n;
-            const int r = p / CH, c = p % CH;
-            const int pos = j * B + r;
-            stage[n] = pos < T ? *(const u32x4 *)(kb + (size_t)pos * row_stride + c * 8)
-                               : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto store_tile = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int n = 0; n < NCH; ++n) {
-            const int p = tid + 256 * n;
-            const int r = p / CH, c = p % CH;
-            *(u32x4 *)(lds[buf] + r * (D * 2) + ((c ^ ((r / S) & (CH - 1))) << 4)) = stage[n];
-        }
-    };
     // A operand: lane l holds reshaped key column cc = l%16 at k index
-    // kk*32 + 8*(l/16): key row cc S + s, chunk e / 8 (s = k / D, e = k % D)
+    // kk*32 + 8*(l/16): key row cc S + s, logical chunk e / 8 with s = kk*32 / D
+    // and e / 8 = 4 (kk mod NQ) + l/16.  The swizzle depends on cc only, so the
+    // per-lane offset takes NQ values and s adds a constant.
+    uint32_t aoff[NQ];
+#pragma unroll
+    for (int m = 0; m < NQ; ++m)
+        aoff[m] = (uint32_t)(a_loc * S * D * 2) + (uint32_t)(((4 * m + kq) ^ (a_loc & (CH - 1))) << 4);
     auto block_product = [&](const char *t) __attribute__((always_inline)) {
         f32x4 acc[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 ab[LK];
+        auto rd = [&](int kk) __attribute__((always_inline)) {
+            return __builtin_bit_cast(
+                bf16x8, *(const u32x4 *)(t + aoff[kk % NQ] + (kk * 32 / D) * (D * 2)));
+        };
+#pragma unroll
+        for (int kk = 0; kk < LK; ++kk) ab[kk] = rd(kk);
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
-            const int kidx = kk * 32 + 8 * kq;
-            const int s = kidx / D, e = kidx % D;
-            const int r = a_loc * S + s;
-            const bf16x8 av = __builtin_bit_cast(
-                bf16x8, *(const u32x4 *)(t + r * (D * 2) + (((e >> 3) ^ (a_loc & (CH - 1))) << 4)));
-            acc[kk & 3] = mfma16(av, qr[kk], acc[kk & 3]);
+            acc[kk & 3] = mfma16(ab[kk % LK], qr[kk], acc[kk & 3]);
+            if (kk + LK < NK) ab[kk % LK] = rd(kk + LK);
+            __builtin_amdgcn_sched_barrier(0);
         }
         return (acc[0] + acc[1]) + (acc[2] + acc[3]);
     };
 
-    // pass 0: per-lane running max / sum (log2 domain) over the lane's values;
-    // pass 1: per key block, sum of 2^(A - lse) over the 16 x 16 tile
     float m_l = -INFINITY, l_l = 0.0f, lse_row = 0.0f;
+    // pass 1: the score of key block j is kept by lane j % 64 and stored 64 at
+    // a time, so no store sits between a tile's copies and the wait for them
+    float stash = 0.0f;
     float *srow = scores + (((size_t)b * hq + h) * nqb + i) * nqb;
-    for (int pass = 0; pass < 2; ++pass) {
-        load_tile(0);
-        store_tile(0);
-        __syncthreads();
-        for (int j = 0; j <= i; ++j) {
-            if (j < i) load_tile(j + 1);
-            const f32x4 c = block_product(lds[j & 1]);
-            // C lane layout: query row a = 16 i + l%16, key columns 16 j + 4 (l/16) + jj
+    // one key block j (tile in t); C lane layout: query row a = 16 i + l%16,
+    // key columns 16 j + 4 (l/16) + jj
+    auto step = [&](auto pass, int j, const char *t) __attribute__((always_inline)) {
+        if (j > i) return;  // uniform: past the causal edge of this wave's block
+        const f32x4 c = block_product(t);
+        float v[4];
+        bool ok[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int cb = j * kXaRows + 4 * kq + jj;
+            ok[jj] = cb <= a && a < Tr;
+            v[jj] = c[jj] * scale_log2;
+        }
+        if constexpr (decltype(pass)::value == 0) {
+            // running max / sum (log2 domain) over the lane's values
+            float mb = -INFINITY;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) mb = ok[jj] ? fmaxf(mb, v[jj]) : mb;
+            const float m_new = fmaxf(m_l, mb);
+            if (m_new != -INFINITY) {
+                float l = l_l * fast_exp2(m_l - m_new);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) l += ok[jj] ? fast_exp2(v[jj] - m_new) : 0.0f;
+                l_l = l;
+                m_l = m_new;
+            }
+        } else {
             float e_sum = 0.0f;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int cb = j * kXaRows + 4 * kq + jj;
-                const bool ok = cb <= a && a < Tr;
-                const float v = c[jj] * scale_log2;
-                if (pass == 0) {
-                    if (ok) {
-                        const float m_new = fmaxf(m_l, v);
-                        l_l = l_l * fast_exp2(m_l - m_new) + fast_exp2(v - m_new);
-                        m_l = m_new;
-                    }
-                } else if (ok) {
-                    e_sum += fast_exp2(v - lse_row);
-                }
+            for (int jj = 0; jj < 4; ++jj) e_sum += ok[jj] ? fast_exp2(v[jj] - lse_row) : 0.0f;
+            e_sum = group_sum<32>(e_sum);
+            e_sum = sum_xor32(e_sum);
+            const int slot = j & 63;
+            if (lane == slot) stash = e_sum;
+            if (slot == 63 || j == i) {  // uniform
+                if (active && lane <= slot) srow[(j & ~63) + lane] = stash;
             }
-            if (pass == 1) {
-                e_sum = group_sum<32>(e_sum);
-                e_sum = sum_xor32(e_sum);
-                if (active && lane == 0) srow[j] = e_sum;
-            }
-            if (j < i) store_tile((j + 1) & 1);
-            __syncthreads();
         }
-        if (pass == 0) {
-            const float M = row4_max(m_l);
-            const float L = row4_sum(m_l == -INFINITY ? 0.0f : l_l * fast_exp2(m_l - M));
-            lse_row = M + fast_log2(L);
+    };
+    auto run_pass = [&](auto pass) __attribute__((always_inline)) {
+        issue_tile(0, lds0);
+        issue_tile(1, lds1);
+        tile_ready(0, lds0);
+        for (int j = 0; j <= j_last; j += 3) {
+            issue_tile(j + 2, lds2);
+            step(pass, j, lds0);
+            tile_ready(j + 1, lds1);
+            if (j + 1 > j_last) break;
+            issue_tile(j + 3, lds0);
+            step(pass, j + 1, lds1);
+            tile_ready(j + 2, lds2);
+            if (j + 2 > j_last) break;
+            issue_tile(j + 4, lds1);
+            step(pass, j + 2, lds2);
+            tile_ready(j + 3, lds0);
         }
+        // drain the copies of tiles past the end before the buffers are reused
+        vm_wait_barrier(ic<0>{});
+    };
+
+    run_pass(ic<0>{});
+    {
+        const float M = row4_max(m_l);
+        const float L = row4_sum(m_l == -INFINITY ? 0.0f : l_l * fast_exp2(m_l - M));
+        lse_row = M + fast_log2(L);
     }
+    run_pass(ic<1>{});
 }
 
 // One workgroup per (query block i, head h, sequence b): the kept-block bits.
@@ -259,11 +381,12 @@ hipError_t launch_scores_t(const XaScoreArgs &a, hipStream_t stream)
     const int hpw = G >= 4 ? 4 : G;
     const int n_hgroups = G / hpw;
     const int n_units = a.batch * a.hkv;
-    const long long n_wg = (long long)a.nqb * n_hgroups * n_units;
+    const int npairs = (a.nqb + 1) / 2;
+    const long long n_wg = (long long)npairs * n_hgroups * n_units;
     if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    xa_score_kernel<D, S><<<(unsigned)n_wg, 256, 0, stream>>>(
+    xa_score_kernel<D, S><<<(unsigned)n_wg, kXaWaves * 64, 0, stream>>>(
         (const uint16_t *)a.q, (const uint16_t *)a.k, a.cu_seqlens, a.hq, a.hkv, G, hpw,
-        n_hgroups, n_units, a.nqb, a.sm_scale / S * kLog2e, a.scores);
+        n_hgroups, n_units, npairs, a.nqb, a.sm_scale / S * kLog2e, a.scores);
     return hipGetLastError();
 }
 
