@@ -50,6 +50,8 @@ def parse():
                    help="skip the batched decode sweep (batch 8/16/24/32 at a 32K context)")
     p.add_argument("--no-chunked", action="store_true",
                    help="skip the chunked prefill (16384-token chunks over a growing key prefix)")
+    p.add_argument("--no-xattn", action="store_true",
+                   help="skip the XAttention sparse-branch timing (scores, selection, masked prefill)")
     p.add_argument("--cpu-rows", type=int, default=192,
                    help="query rows of the FA layer the oracle times (SA gets 4x)")
     p.add_argument("--profile", action="store_true",
@@ -449,6 +451,51 @@ def main():
                    "vs_one_call": round(t_prefill / t_chunked, 3)}
         log("chunked prefill done")
 
+    # ---- XAttention as the sparse branch of one layer at T: antidiagonal scores,
+    # threshold selection and the block-masked prefill, on the i.i.d. inputs and on
+    # locality-structured inputs (a positional code on Q and K, two strengths)
+    xattn = None
+    if not args.no_xattn:
+        XB, XS, XTAU = 128, 8, 0.9
+        nqb = -(-T // XB)
+        nwx = -(-nqb // 32)
+        sc = torch.empty((1, HQ, nqb, nqb), dtype=torch.float32, device=dev)
+        mk = torch.empty((1, HQ, nqb, nwx), dtype=torch.int32, device=dev)
+        xa_flop = 2 * HQ * (nqb * (nqb + 1) // 2) * 16 * 16 * (XS * D) * 2  # two passes
+        xattn = {"block": XB, "stride": XS, "threshold": XTAU, "seq": T,
+                 "fa_layer_ms": round(t_fa * 1e3, 3),
+                 "sa_layer_ms": round(t_sa * 1e3, 3) if sa_layers else None,
+                 "inputs": {}}
+        inputs = [("iid", lambda: sets[0])]
+        for alpha in (2.0, 3.0):
+            inputs.append((f"positional_a{alpha:g}",
+                           lambda a_=alpha: synth.device_positional_qkv(T, HQ, HKV, D, 31, a_)))
+        for name, make in inputs:
+            q, k, v = make()
+            for rep in range(2):  # first run warms up, second is timed
+                e = [ev() for _ in range(4)]
+                e[0].record(stream)
+                _lib.fa_xattn_scores(q, k, cu, T, XB, XS, scale, sc)
+                e[1].record(stream)
+                _lib.fa_xattn_select(sc, cu, XB, XTAU, mk)
+                e[2].record(stream)
+                _lib.fa_attn_prefill_xattn(q, k, v, o_pre, cu, T, XB, mk, scale)
+                e[3].record(stream)
+                torch.cuda.synchronize()
+            t3 = [e[i].elapsed_time(e[i + 1]) for i in range(3)]
+            bits = mk.cpu().numpy().view(np.uint32)
+            kept = int(np.unpackbits(bits.view(np.uint8)).sum())
+            layer = sum(t3)
+            xattn["inputs"][name] = {
+                "density": round(kept / (HQ * nqb * (nqb + 1) // 2), 4),
+                "scores_ms": round(t3[0], 3), "select_ms": round(t3[1], 3),
+                "prefill_ms": round(t3[2], 3), "layer_ms": round(layer, 3),
+                "speedup_vs_fa_layer": round(t_fa * 1e3 / layer, 3),
+                "scores_tflops": round(xa_flop / (t3[0] * 1e-3) / 1e12, 1)}
+            del q, k, v
+        del sc, mk
+        log("xattn branch done")
+
     # ---- roofline --------------------------------------------------------------
     fa_flop = flops_of_pairs(pairs_fa(T))
     sa_flop = flops_of_pairs(pairs_sa(T))
@@ -494,6 +541,7 @@ def main():
             "speedup_vs_all_fa": round(t_prefill_allfa / t_prefill, 3),
             "context_sweep": sweep,
             "chunked_16k": chunked,
+            "xattn_branch": xattn,
         },
         "decode": {
             "tok_s": round(NB / t_decode, 1),

@@ -91,6 +91,40 @@ def block_scores(q, k, cu_seqlens, block, stride, sm_scale, heads=None):
     return out
 
 
+def block_score_row(q_h, k_h, stride, sm_scale, block, i):
+    """x2-x5 for query block i of one head of one sequence, computed on its own
+    (for sampled checks at full length): q_h, k_h [T, d] -> score[i][0..i]
+    (float64, length i + 1).  Only the reshaped rows of block i and the columns
+    they can see are formed."""
+    q_h, k_h = _f64(q_h), _f64(k_h)
+    T, d = q_h.shape
+    Tr = -(-T // stride)
+    R = block // stride
+    a0, a1 = R * i, min(R * i + R, Tr)
+    cols = a1  # reshaped columns 0 .. a1-1 (b <= a)
+
+    def rows_of(x, r0, r1, flip):
+        out = np.zeros(((r1 - r0) * stride, d))
+        p0, p1 = r0 * stride, min(r1 * stride, T)
+        if p1 > p0:
+            out[: p1 - p0] = x[p0:p1]
+        out = out.reshape(r1 - r0, stride, d)
+        if flip:
+            out = out[:, ::-1, :]
+        return out.reshape(r1 - r0, stride * d)
+
+    qr = rows_of(q_h, a0, a1, True)
+    kr = rows_of(k_h, 0, cols, False)
+    A = (qr @ kr.T) * (sm_scale / stride)
+    A[np.arange(cols)[None, :] > np.arange(a0, a1)[:, None]] = -np.inf
+    m = A.max(axis=1, keepdims=True)
+    P = np.exp(A - m)
+    P /= P.sum(axis=1, keepdims=True)
+    Pp = np.zeros((a1 - a0, (i + 1) * R))
+    Pp[:, :cols] = P
+    return Pp.sum(axis=0).reshape(i + 1, R).sum(axis=1)
+
+
 def select_blocks(scores32, seqlens, block, threshold):
     """x6: scores float32 [B, H, NQB, NQB] (as the kernel produced them) ->
     kept-block mask bool [B, H, NQB, NQB]."""
@@ -125,10 +159,9 @@ def attn_prefill(q, k, v, cu_seqlens, keep, block, sm_scale, rows=None):
     """x7: exact softmax attention over the kept blocks.  q [total, Hq, d], k/v
     [total, Hkv, d] (fp32 or bf16 bits), keep bool [B, Hq, NQB, NQB].
     Returns (o float64 [n_rows, Hq, d], lse float64 [n_rows, Hq])."""
-    qf, kf, vf = _f64(q), _f64(k), _f64(v)
     cu = np.asarray(cu_seqlens, np.int64)
-    total, hq, d = qf.shape
-    G = hq // kf.shape[1]
+    total, hq, d = q.shape
+    G = hq // k.shape[1]
     rows = np.arange(total) if rows is None else np.asarray(rows)
     o = np.zeros((len(rows), hq, d))
     lse = np.zeros((len(rows), hq))
@@ -137,11 +170,14 @@ def attn_prefill(q, k, v, cu_seqlens, keep, block, sm_scale, rows=None):
         s0 = int(cu[b])
         t = int(r) - s0
         keys = np.arange(t + 1)
+        # widen only what row r reads: its query and keys s0 .. s0 + t
+        qf = _f64(q[r])
+        kf, vf = _f64(k[s0:s0 + t + 1]), _f64(v[s0:s0 + t + 1])
         for h in range(hq):
             vis = keys[keep[b, h, t // block, keys // block]]
-            sc = kf[s0 + vis, h // G] @ qf[r, h] * sm_scale
+            sc = kf[vis, h // G] @ qf[h] * sm_scale
             m = sc.max()
             p = np.exp(sc - m)
-            o[n, h] = p @ vf[s0 + vis, h // G] / p.sum()
+            o[n, h] = p @ vf[vis, h // G] / p.sum()
             lse[n, h] = m + np.log(p.sum())
     return o, lse

@@ -133,3 +133,33 @@ def device_normal(shape, seed: int, dtype_name: str = "bf16", device: str = "cud
     if scale != 1.0:
         t.mul_(scale)
     return t.to(dt)
+
+
+def device_positional_qkv(T: int, hq: int, hkv: int, d: int, seed: int, alpha: float,
+                          device: str = "cuda:0"):
+    """Locality-structured bf16 Q, K, V [T, heads, d] drawn on the device.
+
+    Q and K are N(0,1) plus alpha times a sinusoidal position code on their first
+    32 dims: [cos(t w_i), sin(t w_i)], w_i = 2 pi / (64 * 2^i), i = 0..15.  The
+    code's dot product between positions t and s is alpha^2 * sum_i cos((t-s) w_i),
+    largest at t = s and decaying with distance, so attention mass concentrates
+    on nearby keys the way it does in trained long-context models; V is N(0,1).
+    Drawn in the order Q, K, V from one seeded generator."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    t = torch.arange(T, device=device, dtype=torch.float32)[:, None]
+    w = 2 * math.pi / (64.0 * 2.0 ** torch.arange(16, device=device, dtype=torch.float32))
+    pe = torch.cat([torch.cos(t * w), torch.sin(t * w)], dim=1)  # [T, 32]
+
+    def draw(h, with_pe):
+        x = torch.randn((T, h, d), generator=g, device=device, dtype=torch.float32)
+        if with_pe:
+            x[:, :, :32] += alpha * pe[:, None, :]
+        return x.to(torch.bfloat16)
+
+    q = draw(hq, True)
+    k = draw(hkv, True)
+    v = draw(hkv, False)
+    return q, k, v

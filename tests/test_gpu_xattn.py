@@ -177,3 +177,48 @@ def test_xattn_prefill_with_every_block_kept_is_the_fa_kernel(block):
     torch.cuda.synchronize()
     assert np.array_equal(o, o_fa.view(torch.int16).cpu().numpy().view(np.uint16))
     assert np.array_equal(lse, l_fa.cpu().numpy())
+
+
+def test_full_size_llama_128k_sampled():
+    """A 131072-token Llama-shaped layer (32 q / 8 kv heads, d 128, bf16; block
+    128, stride 8, threshold 0.9) on locality-structured inputs, launched as the
+    benchmark launches it.  Every (head, query block) row of scores must sum to
+    the block's 16 reshaped rows (each row's softmax sums to 1); sampled rows
+    match the oracle's per-block scores; their selections are bit-exact against
+    the oracle's on the GPU's scores; sampled output rows of the masked prefill
+    match the oracle over the GPU's mask."""
+    T, hq, hkv, d, block, stride, tau = 131072, 32, 8, 128, 128, 8, 0.9
+    scale = 1 / math.sqrt(d)
+    q, k, v = synth.device_positional_qkv(T, hq, hkv, d, seed=31, alpha=3.0)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=DEV)
+    nqb = T // block
+    nw = nqb // 32
+    sc = torch.empty((1, hq, nqb, nqb), dtype=torch.float32, device=DEV)
+    m = torch.empty((1, hq, nqb, nw), dtype=torch.int32, device=DEV)
+    o = torch.empty_like(q)
+    lse = torch.empty((T, hq), dtype=torch.float32, device=DEV)
+    _lib.fa_xattn_scores(q, k, cu, T, block, stride, scale, sc)
+    _lib.fa_xattn_select(sc, cu, block, tau, m)
+    _lib.fa_attn_prefill_xattn(q, k, v, o, cu, T, block, m, scale, lse=lse)
+    torch.cuda.synchronize()
+    got = sc.cpu().numpy()[0]
+    tri = np.tril(np.ones((nqb, nqb), bool))
+    row_sums = np.where(tri, got, 0.0).sum(axis=-1, dtype=np.float64)
+    assert np.abs(row_sums - 16.0).max() <= 2e-3
+    qh = q.view(torch.int16).cpu().numpy().view(np.uint16)
+    kh = k.view(torch.int16).cpu().numpy().view(np.uint16)
+    vh = v.view(torch.int16).cpu().numpy().view(np.uint16)
+    keep = unpack(m.cpu().numpy(), nqb)
+    for h, i in [(0, 0), (0, 1), (5, 300), (13, 511), (31, 1023), (22, 1022)]:
+        ref = xattn.block_score_row(qh[:, h], kh[:, h // (hq // hkv)], stride, scale, block, i)
+        assert np.abs(got[h, i, : i + 1] - ref).max() <= 1e-4, (h, i)
+        one = np.zeros((1, 1, i + 1, i + 1), np.float32)
+        one[0, 0, i] = got[h, i, : i + 1]
+        want = xattn.select_blocks(one, [(i + 1) * block], block, tau)[0, 0, i]
+        assert np.array_equal(keep[0, h, i, : i + 1], want), (h, i)
+        assert not keep[0, h, i, i + 1:].any(), (h, i)
+    rows = [0, 127, 128, 65537, T - 1]
+    o_ref, l_ref = xattn.attn_prefill(qh, kh, vh, [0, T], keep, block, scale, rows=rows)
+    oh = synth.bf16_bits_to_f32(o.view(torch.int16).cpu().numpy().view(np.uint16)[rows])
+    assert np.abs(oh.astype(np.float64) - o_ref).max() <= 2e-2
+    assert np.abs(lse.cpu().numpy()[rows] - l_ref).max() <= 1e-3

@@ -152,3 +152,17 @@ def test_block_scores_gqa_equal_repeated_kv():
     np.testing.assert_array_equal(a, b)
     assert not np.allclose(a[0, 1], xattn.block_scores(q, np.repeat(k[:, ::-1], 2, axis=1),
                                                        [0, T], B, S, 0.25)[0, 1])
+
+
+@pytest.mark.parametrize("T,stride,block", [(700, 8, 128), (450, 4, 64), (129, 8, 128)])
+def test_single_block_row_agrees_with_the_pinned_full_scores(T, stride, block):
+    """The per-block score function (used for sampled checks at full length) agrees
+    with the whole-matrix scores pinned above, on every query block."""
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((T, 2, 16))
+    k = rng.standard_normal((T, 1, 16))
+    full = xattn.block_scores(q, k, [0, T], block, stride, 0.25)
+    for i in range(-(-T // block)):
+        for h in range(2):
+            row = xattn.block_score_row(q[:, h], k[:, 0], stride, 0.25, block, i)
+            np.testing.assert_allclose(row, full[0, h, i, : i + 1], rtol=1e-12, atol=1e-13)
