@@ -52,6 +52,8 @@ def parse():
                    help="skip the chunked prefill (16384-token chunks over a growing key prefix)")
     p.add_argument("--no-xattn", action="store_true",
                    help="skip the XAttention sparse-branch timing (scores, selection, masked prefill)")
+    p.add_argument("--no-triangle", action="store_true",
+                   help="skip the Triangle Attention sparse-branch timing")
     p.add_argument("--cpu-rows", type=int, default=192,
                    help="query rows of the FA layer the oracle times (SA gets 4x)")
     p.add_argument("--profile", action="store_true",
@@ -86,6 +88,16 @@ def pairs_sa(T: int, sink=SINK, window=WINDOW, block=BLOCK) -> int:
         # rows of block i see `full` whole blocks and 1..rows keys of their own block
         n += rows * full * block + rows * (rows + 1) // 2
     return n
+
+
+def pairs_ta(T: int, last_q: int, sink=SINK, window=WINDOW, block=BLOCK) -> int:
+    """Visible pairs of one Triangle Attention sequence: the SA rows, plus every
+    causal pair of the rows in the last last_q // block query blocks."""
+    nqb = -(-T // block)
+    tail0 = max(0, nqb - last_q // block) * block
+    if tail0 >= T:
+        return pairs_sa(T, sink, window, block)
+    return pairs_sa(tail0, sink, window, block) + pairs_fa(T) - pairs_fa(tail0)
 
 
 def flops_of_pairs(p: int) -> float:
@@ -496,6 +508,34 @@ def main():
         del sc, mk
         log("xattn branch done")
 
+    # ---- Triangle Attention as the sparse branch of one layer at T: the streaming
+    # sink + window blocks plus a dense tail of the last query blocks
+    tri = None
+    if not args.no_triangle:
+        r1 = np.zeros((1, 1), np.uint8)
+        r1_dev = torch.from_numpy(r1).to(dev)
+        q, k, v = sets[0]
+        tri = {"seq": T, "sink": SINK, "window": WINDOW, "block": BLOCK,
+               "fa_layer_ms": round(t_fa * 1e3, 3),
+               "sa_layer_ms": round(t_sa * 1e3, 3) if sa_layers else None, "tails": []}
+        for last_q in (128, 1024):
+            ms = None
+            for rep in range(3):  # first call warms up; the best of two timed calls
+                a, b_ = ev(), ev()
+                a.record(stream)
+                _lib.fa_attn_prefill_triangle(q, k, v, o_pre, cu, T, r1_dev, 0, SINK, WINDOW,
+                                              BLOCK, last_q, scale, route_host=r1)
+                b_.record(stream)
+                torch.cuda.synchronize()
+                if rep:
+                    ms = min(ms or 1e30, a.elapsed_time(b_))
+            fl = flops_of_pairs(pairs_ta(T, last_q))
+            tri["tails"].append({"last_q": last_q, "ms": round(ms, 3),
+                                 "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                                 "pairs_vs_fa": round(pairs_ta(T, last_q) / pairs_fa(T), 5),
+                                 "speedup_vs_fa_layer": round(t_fa * 1e3 / ms, 2)})
+        log("triangle branch done")
+
     # ---- roofline --------------------------------------------------------------
     fa_flop = flops_of_pairs(pairs_fa(T))
     sa_flop = flops_of_pairs(pairs_sa(T))
@@ -542,6 +582,7 @@ def main():
             "context_sweep": sweep,
             "chunked_16k": chunked,
             "xattn_branch": xattn,
+            "triangle_branch": tri,
         },
         "decode": {
             "tok_s": round(NB / t_decode, 1),

@@ -204,6 +204,37 @@ fa_status fa_attn_prefill_kv(const void *q, const void *k, const void *v, void *
                              int32_t window_tokens, int32_t block_tokens,
                              float sm_scale, void *stream);
 
+/*
+ * fa_attn_prefill_triangle -- fa_attn_prefill with Triangle Attention as the
+ * sparse branch: the pages use TriangleMix's Triangle Attention (TA), a fixed,
+ * training-free triangle-shaped block topology for prefill, as a sparse
+ * backend of the router [thelatestinai paper page, Table 3, Table 5 and its
+ * caption, Table 12].  They give no steps; the published topology is read as:
+ * a query block of an SA sequence keeps its sink and window blocks exactly as
+ * in fa_attn_prefill, and every query block among the last last_q_tokens /
+ * block_tokens blocks of the sequence keeps every key block (the dense rows at
+ * the bottom of the causal triangle).  FA-routed sequences are plain causal
+ * attention.  last_q_tokens = 0 is fa_attn_prefill; a value covering the
+ * sequence makes it FA.  Decode of such a layer is the FA decode: the decoded
+ * token lies in the dense tail.
+ *
+ * Arguments, layouts, kernels and support as fa_attn_prefill; last_q_tokens
+ * is a host int, a non-negative multiple of block_tokens.
+ * Errors: as fa_attn_prefill; a negative last_q_tokens or one not a multiple
+ * of block_tokens -> FA_ERR_INVALID_ARG.
+ */
+fa_status fa_attn_prefill_triangle(const void *q, const void *k, const void *v,
+                                   void *o, float *lse, int32_t dtype,
+                                   const int32_t *cu_seqlens, int32_t batch,
+                                   int32_t max_seqlen, int32_t n_q_heads,
+                                   int32_t n_kv_heads, int32_t head_dim,
+                                   const uint8_t *route,
+                                   const uint8_t *route_host, int32_t n_layers,
+                                   int32_t layer, int32_t sink_tokens,
+                                   int32_t window_tokens, int32_t block_tokens,
+                                   int32_t last_q_tokens, float sm_scale,
+                                   void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* XAttention sparse branch                                                 */
 /* ------------------------------------------------------------------------ */

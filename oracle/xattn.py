@@ -170,11 +170,13 @@ def attn_prefill(q, k, v, cu_seqlens, keep, block, sm_scale, rows=None):
         s0 = int(cu[b])
         t = int(r) - s0
         keys = np.arange(t + 1)
-        # widen only what row r reads: its query and keys s0 .. s0 + t
+        kept = keep[b, :, t // block][:, keys // block]  # [hq, t + 1]: key s visible to head h
+        # widen only what row r reads: its query and the keys some head keeps
+        used = keys[kept.any(axis=0)]
         qf = _f64(q[r])
-        kf, vf = _f64(k[s0:s0 + t + 1]), _f64(v[s0:s0 + t + 1])
+        kf, vf = _f64(k[s0 + used]), _f64(v[s0 + used])
         for h in range(hq):
-            vis = keys[keep[b, h, t // block, keys // block]]
+            vis = kept[h, used]
             sc = kf[vis, h // G] @ qf[h] * sm_scale
             m = sc.max()
             p = np.exp(sc - m)

@@ -23,7 +23,7 @@ EXPORTS = (
     "fa_last_error", "fa_abi_version", "fa_router_workspace_size", "fa_router_decide",
     "fa_block_plan", "fa_attn_prefill", "fa_decode_workspace_size", "fa_attn_decode",
     "fa_kv_compact", "fa_attn_decode_ring", "fa_attn_prefill_kv", "fa_xattn_scores",
-    "fa_xattn_select", "fa_attn_prefill_xattn",
+    "fa_xattn_select", "fa_attn_prefill_xattn", "fa_attn_prefill_triangle",
 )
 
 
@@ -62,6 +62,9 @@ def lib() -> ctypes.CDLL:
     L.fa_attn_prefill_kv.restype = I32
     L.fa_attn_prefill_kv.argtypes = [P, P, P, P, P, I32, P, P, I32, I32, I32, I32, I32, P, P,
                                      I32, I32, I32, I32, I32, F, P]
+    L.fa_attn_prefill_triangle.restype = I32
+    L.fa_attn_prefill_triangle.argtypes = [P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, P, P,
+                                           I32, I32, I32, I32, I32, I32, F, P]
     L.fa_xattn_scores.restype = I32
     L.fa_xattn_scores.argtypes = [P, P, I32, P, I32, I32, I32, I32, I32, I32, I32, F, P, I32, P]
     L.fa_xattn_select.restype = I32
@@ -207,6 +210,23 @@ def fa_attn_prefill_kv(q, k, v, o, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, rou
         _ptr(cu_seqlens_k), batch, int(max_seqlen_q), hq, hkv, d, _ptr(route), rh,
         route.shape[1], layer, sink_tokens, window_tokens, block_tokens, float(sm_scale),
         _stream(stream)))
+    del keep
+
+
+def fa_attn_prefill_triangle(q, k, v, o, cu_seqlens, max_seqlen, route, layer, sink_tokens,
+                             window_tokens, block_tokens, last_q_tokens, sm_scale, lse=None,
+                             route_host=None, stream=None):
+    """Prefill with Triangle Attention as the sparse branch (SA rows plus a dense
+    tail of last_q_tokens rows per sequence): q [total, Hq, d], k/v [total, Hkv, d] -> o."""
+    _require_cuda(q, k, v, o, cu_seqlens, route, lse)
+    batch = cu_seqlens.numel() - 1
+    _, hq, d = q.shape
+    hkv = k.shape[1]
+    keep, rh = _host_u8(route_host)
+    _check(lib().fa_attn_prefill_triangle(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dtype_code(q), _ptr(cu_seqlens), batch,
+        int(max_seqlen), hq, hkv, d, _ptr(route), rh, route.shape[1], layer, sink_tokens,
+        window_tokens, block_tokens, last_q_tokens, float(sm_scale), _stream(stream)))
     del keep
 
 

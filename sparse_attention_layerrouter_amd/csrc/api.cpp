@@ -79,13 +79,16 @@ size_t decode_splits_cap(int max_cache)
     return (size_t)(s > 64 ? s : 64);
 }
 
-// Shared by fa_attn_prefill (queries = keys) and fa_attn_prefill_kv.
+// Shared by fa_attn_prefill (queries = keys), fa_attn_prefill_kv and
+// fa_attn_prefill_triangle (tail_tokens > 0: the last tail_tokens rows of each
+// SA sequence keep every key).
 fa_status prefill_impl(const char *fn, const void *q, const void *k, const void *v, void *o,
                        float *lse, int32_t dtype, const int32_t *cu_q, const int32_t *cu_k,
                        int32_t batch, int32_t max_seqlen, int32_t n_q_heads, int32_t n_kv_heads,
                        int32_t head_dim, const uint8_t *route, const uint8_t *route_host,
                        int32_t n_layers, int32_t layer, int32_t sink_tokens,
-                       int32_t window_tokens, int32_t block_tokens, float sm_scale, void *stream)
+                       int32_t window_tokens, int32_t block_tokens, int32_t tail_tokens,
+                       float sm_scale, void *stream)
 {
     if (!q || !k || !v || !o || !cu_q || !route)
         return fail(FA_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
@@ -104,6 +107,11 @@ fa_status prefill_impl(const char *fn, const void *q, const void *k, const void 
     if (!sparse_cfg(sink_tokens, window_tokens, block_tokens, a.ns, a.nw, a.bk_log2))
         return fail(FA_ERR_INVALID_ARG, "%s: bad sparse config sink=%d window=%d block=%d", fn,
                     sink_tokens, window_tokens, block_tokens);
+    if (tail_tokens < 0 || tail_tokens % block_tokens != 0)
+        return fail(FA_ERR_INVALID_ARG,
+                    "%s: last_q_tokens=%d must be a non-negative multiple of block=%d", fn,
+                    tail_tokens, block_tokens);
+    a.nl = tail_tokens / block_tokens;
     if (dtype != FA_F32 && dtype != FA_BF16)
         return fail(FA_ERR_UNSUPPORTED, "%s: dtype %d is not FA_F32/FA_BF16", fn, dtype);
     if (head_dim != 64 && head_dim != 128)
@@ -135,7 +143,7 @@ extern "C" {
 
 const char *fa_last_error(void) { return g_last_error.c_str(); }
 
-int32_t fa_abi_version(void) { return 5; }
+int32_t fa_abi_version(void) { return 6; }
 
 size_t fa_router_workspace_size(int32_t batch, int32_t hidden, int32_t router_hidden)
 {
@@ -221,7 +229,22 @@ fa_status fa_attn_prefill(const void *q, const void *k, const void *v, void *o, 
 {
     return prefill_impl("fa_attn_prefill", q, k, v, o, lse, dtype, cu_seqlens, cu_seqlens, batch,
                         max_seqlen, n_q_heads, n_kv_heads, head_dim, route, route_host, n_layers,
-                        layer, sink_tokens, window_tokens, block_tokens, sm_scale, stream);
+                        layer, sink_tokens, window_tokens, block_tokens, 0, sm_scale, stream);
+}
+
+fa_status fa_attn_prefill_triangle(const void *q, const void *k, const void *v, void *o,
+                                   float *lse, int32_t dtype, const int32_t *cu_seqlens,
+                                   int32_t batch, int32_t max_seqlen, int32_t n_q_heads,
+                                   int32_t n_kv_heads, int32_t head_dim, const uint8_t *route,
+                                   const uint8_t *route_host, int32_t n_layers, int32_t layer,
+                                   int32_t sink_tokens, int32_t window_tokens,
+                                   int32_t block_tokens, int32_t last_q_tokens, float sm_scale,
+                                   void *stream)
+{
+    return prefill_impl("fa_attn_prefill_triangle", q, k, v, o, lse, dtype, cu_seqlens,
+                        cu_seqlens, batch, max_seqlen, n_q_heads, n_kv_heads, head_dim, route,
+                        route_host, n_layers, layer, sink_tokens, window_tokens, block_tokens,
+                        last_q_tokens, sm_scale, stream);
 }
 
 fa_status fa_attn_prefill_kv(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -236,7 +259,7 @@ fa_status fa_attn_prefill_kv(const void *q, const void *k, const void *v, void *
         return fail(FA_ERR_INVALID_ARG, "fa_attn_prefill_kv: a required pointer is NULL");
     return prefill_impl("fa_attn_prefill_kv", q, k, v, o, lse, dtype, cu_seqlens_q, cu_seqlens_k,
                         batch, max_seqlen_q, n_q_heads, n_kv_heads, head_dim, route, route_host,
-                        n_layers, layer, sink_tokens, window_tokens, block_tokens, sm_scale,
+                        n_layers, layer, sink_tokens, window_tokens, block_tokens, 0, sm_scale,
                         stream);
 }
 

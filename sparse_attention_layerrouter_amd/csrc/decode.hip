@@ -681,7 +681,7 @@ bool decode_g_supported(int G) { return G == 1 || G == 2 || G == 4 || G == 8 || 
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
 {
-    SparseRule r{a.ns, a.nw, a.bk_log2};
+    SparseRule r{a.ns, a.nw, a.bk_log2, 0};
     const float scale_log2 = a.sm_scale * kLog2e;
     hipError_t e;
     if (a.bf16)
@@ -741,7 +741,7 @@ template <typename TE, int D>
 hipError_t launch_compact_t(const CompactArgs &a, hipStream_t stream)
 {
     constexpr int ROWS = 256 / (D / (16 / sizeof(TE)));
-    SparseRule r{a.ns, a.nw, a.bk_log2};
+    SparseRule r{a.ns, a.nw, a.bk_log2, 0};
     dim3 grid((a.ring + ROWS - 1) / ROWS, a.batch * a.hkv);
     kv_compact_kernel<TE, D><<<grid, 256, 0, stream>>>((const TE *)a.k, (const TE *)a.v,
                                                         a.cu_seqlens, a.hkv, r, (TE *)a.k_ring,

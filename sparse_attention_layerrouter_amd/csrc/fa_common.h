@@ -124,7 +124,18 @@ struct SparseRule {
     int ns;       // sink blocks
     int nw;       // window blocks (including the query's own block)
     int bk_log2;  // log2(block tokens)
+    int nl;       // Triangle attention: the last nl query blocks of a sequence keep
+                  // every key block; 0 for the streaming rule
 };
+
+// First position of the dense tail of a sequence of T tokens under the rule
+// (T when the rule has none): rows at or past it keep every earlier key.
+__device__ __forceinline__ int dense_tail_start(int T, const SparseRule &r)
+{
+    if (r.nl <= 0) return T;
+    const int nb = (T + (1 << r.bk_log2) - 1) >> r.bk_log2;
+    return max(0, nb - r.nl) << r.bk_log2;
+}
 
 // Key s visible from query t (positions inside one sequence).
 __device__ __forceinline__ bool visible(int t, int s, bool fa, const SparseRule &r)

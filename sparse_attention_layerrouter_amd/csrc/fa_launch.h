@@ -54,6 +54,7 @@ struct PrefillArgs {
     const uint8_t *route;
     int n_layers, layer;
     int ns, nw, bk_log2;
+    int nl;  // Triangle attention: dense tail blocks per sequence (0: streaming SA)
     float sm_scale;
     int mode;  // kModeMixed / kModeFA / kModeSA / kModeXA
     // kModeXA: kept-block bits [batch][hq][xa_nqb][xa_nw]; the block size is 1 << bk_log2

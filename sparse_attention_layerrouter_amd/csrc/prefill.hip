@@ -211,10 +211,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const bool is_fa = MODE == kModeFA || MODE == kModeXA ? true
                        : MODE == kModeSA ? false
                                          : route[(size_t)b * n_layers + layer] != 0;
+    // Triangle attention: rows at or past tail0 keep every key (the whole
+    // sequence when is_fa); otherwise only the sink and window blocks
+    const int tail0 = is_fa ? 0 : dense_tail_start(T, rule);
 
     const int pw0 = p0 + grp * gpos + (wq % wph) * 32;  // this wave's first position
     const bool wave_active = pw0 < T;
     const int pw_last = min(pw0 + 31, T - 1);  // last valid position of the wave
+    // (is_fa first: FA and XA kernels fold every dense-tail test away)
+    const bool w_dense_any = is_fa || pw_last >= tail0;  // some row of the wave keeps every key
+    const bool w_dense_all = is_fa || pw0 >= tail0;      // every row does
 
     // ---- KV tile schedule: [0, nA) then [tB0, tB0 + nB); in mode XA the kept
     // blocks of the workgroup's query block (all its positions lie in one block),
@@ -253,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         n_tiles = __builtin_amdgcn_readfirstlane(xa_pre[xa_nw]) << (rule.bk_log2 - 6);
     } else {
         int a_end, b_begin;
-        kept_ranges(p0, p1, is_fa, rule, a_end, b_begin);
+        kept_ranges(p0, p1, is_fa || p1 - 1 >= tail0, rule, a_end, b_begin);
         nA = (a_end + kBN - 1) / kBN;
         tB0 = max(nA, b_begin / kBN);
         const int tB1 = (p1 + kBN - 1) / kBN;
@@ -308,6 +314,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int win_lo_max = ((pw_last >> rule.bk_log2) - rule.nw + 1) << rule.bk_log2;
     const int my_t = min(pw0 + l32, T - 1);  // query position of this lane's row
     const int my_win_lo = ((my_t >> rule.bk_log2) - rule.nw + 1) << rule.bk_log2;
+    const bool my_dense = is_fa || my_t >= tail0;
     // does any row of this wave see a key of the tile at k0?
     auto wave_sees = [&](int k0) __attribute__((always_inline)) {
         if constexpr (XA) {  // this wave's head kept the tile's block
@@ -316,7 +323,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                    ((xa_head[wq / wph][blk >> 5] >> (blk & 31)) & 1u) != 0;
         } else {
             return wave_active && k0 <= pw_last &&
-                   (is_fa || k0 < sink_tok || k0 + kBN > win_lo_min);
+                   (w_dense_any || k0 < sink_tok || k0 + kBN > win_lo_min);
         }
     };
 
@@ -455,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         const int k0 = tile_k0(t);
         // mask (causal diagonal, window lower edge, sequence tail)
         const bool need_mask = (k0 + kBN - 1 > pw0) ||
-                               (!is_fa && k0 < win_lo_max && k0 + kBN > sink_tok);
+                               (!w_dense_all && k0 < win_lo_max && k0 + kBN > sink_tok);
         if (need_mask) {
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -463,7 +470,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                 for (int j = 0; j < 16; ++j) {
                     int key = k0 + kb2 * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
                     bool vis = key <= my_t &&
-                               (is_fa || key < sink_tok || key >= my_win_lo);
+                               (my_dense || key < sink_tok || key >= my_win_lo);
                     if (!vis) s[kb2][j] = -INFINITY;
                 }
         }
@@ -653,13 +660,15 @@ __global__ __launch_bounds__(64) void prefill_generic_kernel(
         acc[c] = 0.0f;
     }
     float m = -INFINITY, l = 0.0f;
+    // Triangle attention: rows at or past tail0 keep every key
+    const int tail0 = is_fa ? 0 : dense_tail_start(T, rule);
     int a_end, b_begin;
-    kept_ranges(p0, p1, is_fa, rule, a_end, b_begin);
+    kept_ranges(p0, p1, is_fa || p1 - 1 >= tail0, rule, a_end, b_begin);
     for (int pass = 0; pass < 2; ++pass) {
         int s0 = pass == 0 ? 0 : b_begin;
         int s1 = pass == 0 ? a_end : p1;
         for (int s = s0; s < s1; ++s) {
-            if (!visible(t, s, is_fa, rule)) continue;
+            if (!visible(t, s, is_fa || t >= tail0, rule)) continue;
             if constexpr (MODE == kModeXA) {
                 const int blk = s >> rule.bk_log2;
                 if (((xrow[blk >> 5] >> (blk & 31)) & 1u) == 0) continue;
@@ -752,7 +761,7 @@ hipError_t launch_mode(const PrefillArgs &a, hipStream_t stream, const SparseRul
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream)
 {
-    SparseRule r{a.ns, a.nw, a.bk_log2};
+    SparseRule r{a.ns, a.nw, a.bk_log2, a.nl};
     const float scale_log2 = a.sm_scale * kLog2e;
     switch (a.mode) {
     case kModeFA: return launch_mode<kModeFA>(a, stream, r, scale_log2);

@@ -162,7 +162,7 @@ hipError_t launch_router(const RouterArgs &a, hipStream_t stream)
 
 hipError_t launch_block_plan(const PlanArgs &a, hipStream_t stream)
 {
-    SparseRule r{a.ns, a.nw, a.bk_log2};
+    SparseRule r{a.ns, a.nw, a.bk_log2, 0};
     dim3 g((a.max_qblocks + 255) / 256, a.batch);
     block_plan_kernel<<<g, 256, 0, stream>>>(a.cu_seqlens, a.batch, a.max_qblocks, a.route,
                                              a.n_layers, a.layer, r, a.plan);

@@ -27,14 +27,14 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     assert set(names) == set(_lib.EXPORTS)
     for name in names:
         assert hasattr(L, name), name
 
 
 def test_abi_version_and_clean_error_state():
-    assert _lib.fa_abi_version() == 5
+    assert _lib.fa_abi_version() == 6
 
 
 def test_workspace_sizes():
@@ -99,6 +99,25 @@ def prefill_kv_args(cu_k=P, **kw):
 def test_prefill_kv_validation(kw, status):
     assert _lib.lib().fa_attn_prefill_kv(*prefill_kv_args(**kw)) == status
     assert _lib.last_error().startswith("fa_attn_prefill_kv")
+
+
+def prefill_triangle_args(last_q=128, **kw):
+    a = prefill_args(**kw)
+    return a[:19] + [last_q] + a[19:]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(last_q=-64), _lib.FA_ERR_INVALID_ARG),
+    (dict(last_q=100), _lib.FA_ERR_INVALID_ARG),    # not a multiple of the block
+    (dict(q=None), _lib.FA_ERR_INVALID_ARG),
+    (dict(window=100), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), _lib.FA_ERR_INVALID_ARG),
+    (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), _lib.FA_ERR_UNSUPPORTED),
+])
+def test_prefill_triangle_validation(kw, status):
+    assert _lib.lib().fa_attn_prefill_triangle(*prefill_triangle_args(**kw)) == status
+    assert _lib.last_error().startswith("fa_attn_prefill_triangle")
 
 
 def decode_args(**kw):
