@@ -348,7 +348,7 @@ def main():
             ms = {}
             for kind in ("full", "ring"):
                 times = []
-                for rep in range(3):
+                for rep in range(6):  # one warm-up pass, the median of five timed passes
                     a, b_ = ev(), ev()
                     a.record(stream)
                     for l in range(n_dec_layers):
@@ -367,11 +367,11 @@ def main():
                     torch.cuda.synchronize()
                     if rep:
                         times.append(a.elapsed_time(b_))
-                ms[kind] = float(np.mean(times))
+                ms[kind] = float(np.median(times))
             # the all-FA reference on the same caches
             r_fa = torch.ones((bs, N_LAYERS), dtype=torch.uint8, device=dev)
             times = []
-            for rep in range(3):
+            for rep in range(6):
                 a, b_ = ev(), ev()
                 a.record(stream)
                 for l in range(n_dec_layers):
@@ -384,7 +384,7 @@ def main():
                 torch.cuda.synchronize()
                 if rep:
                     times.append(a.elapsed_time(b_))
-            ms_fa = float(np.mean(times))
+            ms_fa = float(np.median(times))
             kv_full_s = 2 * n_dec_layers * bs * HKV * SC * D * 2
             kv_ring_s = sum(2 * bs * HKV * (RING if l in rings32 else SC) * D * 2
                             for l in range(n_dec_layers))
