@@ -121,3 +121,21 @@ def test_full_size_llama_128k_sampled():
     oh = as_f64(host_of(o)[rows])
     assert np.abs(oh - o_ref).max() <= 2e-2
     assert np.abs(lse.cpu().numpy()[rows] - l_ref).max() <= 1e-3
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_empty_and_short_sequences(bf16):
+    """A zero-length sequence, one shorter than the tail and one shorter than a
+    block, beside a normal one."""
+    rng = np.random.default_rng(29)
+    lengths, hq, hkv, d = [700, 0, 40, 130], 8, 2, 128
+    block, sink, window, last_q = 64, 64, 128, 128
+    cu = synth.cu_seqlens_of(lengths)
+    q, k, v = synth.qkv_host(rng, int(cu[-1]), hq, hkv, d, bf16=bf16)
+    routes = [0, 0, 0, 0]
+    o, lse = run(_lib.fa_attn_prefill_triangle, q, k, v, cu, routes, sink, window, block, 0.09,
+                 last_q)
+    o_ref, l_ref = triangle.attn_prefill(q, k, v, cu, routes, block, sink, window, last_q, 0.09)
+    tol, tol_lse = (2e-2, 1e-3) if bf16 else (1e-4, 1e-4)
+    assert np.abs(as_f64(o) - o_ref).max() <= tol
+    assert np.abs(lse - l_ref).max() <= tol_lse

@@ -222,3 +222,33 @@ def test_full_size_llama_128k_sampled():
     oh = synth.bf16_bits_to_f32(o.view(torch.int16).cpu().numpy().view(np.uint16)[rows])
     assert np.abs(oh.astype(np.float64) - o_ref).max() <= 2e-2
     assert np.abs(lse.cpu().numpy()[rows] - l_ref).max() <= 1e-3
+
+
+def test_empty_sequence_in_the_batch():
+    """A zero-length sequence gets no scores, an all-zero mask row set and no
+    output rows; its neighbours match the oracle as if it were absent."""
+    rng = np.random.default_rng(17)
+    lengths, hq, hkv, d, block, stride = [300, 0, 200], 8, 2, 128, 128, 8
+    cu = synth.cu_seqlens_of(lengths)
+    q, k, v = synth.qkv_host(rng, int(cu[-1]), hq, hkv, d, bf16=True)
+    scale = 1 / math.sqrt(d)
+    nqb = -(-max(lengths) // block)
+    sc = run_scores(q, k, cu, block, stride, scale, nqb)   # filled with -1 first
+    got = sc.cpu().numpy()
+    assert (got[1] == -1.0).all()                           # nothing written for it
+    ref = xattn.block_scores(q, k, cu, block, stride, scale)
+    for b in (0, 2):
+        nb = -(-lengths[b] // block)
+        tri = np.tril(np.ones((nb, nb), bool))
+        assert np.abs(got[b][:, :nb, :nb][:, tri] - ref[b][:, :nb, :nb][:, tri]).max() <= 1e-4
+    nw = -(-nqb // 32)
+    m = torch.full((3, hq, nqb, nw), -1, dtype=torch.int32, device=DEV)
+    _lib.fa_xattn_select(sc, torch.tensor(cu, device=DEV), block, 0.9, m)
+    torch.cuda.synchronize()
+    words = m.cpu().numpy()
+    assert (words[1] == 0).all()
+    keep = unpack(words, nqb)
+    o, lse = run_xattn_prefill(q, k, v, cu, block, words, scale)
+    o_ref, l_ref = xattn.attn_prefill(q, k, v, cu, keep, block, scale)
+    assert np.abs(as_f64(o) - o_ref).max() <= 2e-2
+    assert np.abs(lse - l_ref).max() <= 1e-3
