@@ -104,11 +104,13 @@ struct TileLoader {
         }
     }
 
-    // descriptor of rows k0 .. T-1 of one KV head
+    // descriptor of rows k0 .. T-1 of one KV head (an empty range when k0 >= T:
+    // in mode XA the second 64-key tile of a sequence's last block can start
+    // past its end, and a negative count would lift the range check)
     static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint16_t *__restrict__ base,
                                                                size_t row_stride, int k0, int T)
     {
-        const long long bytes = (long long)(T - k0) * (long long)row_stride * 2;
+        const long long bytes = (long long)max(T - k0, 0) * (long long)row_stride * 2;
         return __builtin_amdgcn_make_buffer_rsrc((void *)(base + (size_t)k0 * row_stride), (short)0,
                                                  (int)min(bytes, 0x7fffffffLL), kRsrcWord3);
     }

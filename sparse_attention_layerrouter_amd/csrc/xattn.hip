@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kXaWaves * 64) void xa_score_kernel(
     // the copies are unconditional and every wave has NI of them per tile.
     auto issue_tile = [&](int jt, char *dst) __attribute__((always_inline)) {
         const long long bytes =
-            jt <= j_last ? (long long)(T - jt * B) * (long long)row_stride * 2 : 0LL;
+            jt <= j_last ? (long long)max(T - jt * B, 0) * (long long)row_stride * 2 : 0LL;
         const i32x4 rs =
             raw_rsrc(kb + (size_t)jt * B * row_stride, (int)min(bytes, 0x7fffffffLL));
         const uint32_t lds = (uint32_t)(uintptr_t)(lds_void *)dst + wave * NI * 1024;

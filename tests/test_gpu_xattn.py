@@ -252,3 +252,39 @@ def test_empty_sequence_in_the_batch():
     o_ref, l_ref = xattn.attn_prefill(q, k, v, cu, keep, block, scale)
     assert np.abs(as_f64(o) - o_ref).max() <= 2e-2
     assert np.abs(lse - l_ref).max() <= 1e-3
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_tile_past_the_sequence_end_reads_nothing(bf16):
+    """The masked prefill walks a kept 128-token block as two 64-key tiles; when
+    a sequence ends in the first tile, the second starts past its end and must
+    read nothing.  K and V sit at the start of NaN-filled buffers, so a read past
+    the last sequence would turn the (zero-weighted) V rows into NaN outputs."""
+    rng = np.random.default_rng(23)
+    lengths, hq, hkv, d, block = [300, 40, 1], 8, 2, 128, 128
+    cu = synth.cu_seqlens_of(lengths)
+    total = int(cu[-1])
+    q, k, v = synth.qkv_host(rng, total, hq, hkv, d, bf16=bf16)
+    nqb = -(-max(lengths) // block)
+    keep = rng.random((len(lengths), hq, nqb, nqb)) < 0.6
+    idx = np.arange(nqb)
+    keep[..., idx, idx] = True
+    keep &= np.tril(np.ones((nqb, nqb), bool))
+    qd = dev_from(q)
+    kd0, vd0 = dev_from(k), dev_from(v)
+    kbig = torch.full((total + 512, hkv, d), float("nan"), dtype=kd0.dtype, device=DEV)
+    vbig = torch.full((total + 512, hkv, d), float("nan"), dtype=vd0.dtype, device=DEV)
+    kbig[:total] = kd0
+    vbig[:total] = vd0
+    o = torch.empty_like(qd)
+    lse = torch.empty((total, hq), dtype=torch.float32, device=DEV)
+    _lib.fa_attn_prefill_xattn(qd, kbig[:total], vbig[:total], o, torch.tensor(cu, device=DEV),
+                               max(lengths), block, torch.tensor(pack(keep), device=DEV), 0.09,
+                               lse=lse)
+    torch.cuda.synchronize()
+    t = o.contiguous()
+    oh = t.view(torch.int16).cpu().numpy().view(np.uint16) if bf16 else t.cpu().numpy()
+    o_ref, l_ref = xattn.attn_prefill(q, k, v, cu, keep, block, 0.09)
+    got = as_f64(oh)
+    assert np.isfinite(got).all() and np.isfinite(lse.cpu().numpy()).all()
+    assert np.abs(got - o_ref).max() <= (2e-2 if bf16 else 1e-4)
