@@ -139,8 +139,8 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the routed attention step has no multi-GPU "
-              "path in this build (heads and sequences shard with no exchange; see the "
-              "design notes). Run with --gpus 1.", file=sys.stderr)
+              "path (heads and sequences would shard with no exchange). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

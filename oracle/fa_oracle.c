@@ -30,7 +30,7 @@
  * decided in fp32 (the precision the GPU kernel decides it in), and an fp64
  * copy of the logits is returned so callers can report the decision margin.
  *
- * Readings where the pages are silent (all listed in the design doc):
+ * Readings where the pages are silent:
  *   router activation ReLU, strict threshold logit > 0 -> FA (NaN -> SA),
  *   bit 1 = FA; sink and window are counted in tokens and must be multiples of
  *   the block; the window counts whole blocks including the query's own block;

@@ -7,7 +7,7 @@ The pages use TriangleMix's Triangle Attention (TA) as a sparse backend of the
 router: a block-level, fixed ("triangle") topology, training-free, for prefill
 [thelatestinai paper page, Table 3, Table 5 and its caption, Table 12].  They
 print none of its rules, so the published topology is read as follows (readings
-t1..t3 in the design notes):
+labelled t1..t3):
 
   t1  a query block i of a sequence of nb blocks keeps the streaming blocks of
       the SA rule -- the sink blocks j < ns and the window blocks j > i - nw --

@@ -10,7 +10,7 @@ operator with a block selection score used for prefill in the thelatestinai
 paper page's Table 4; the XA columns of its Table 12; and ``find_blocks_chunked``
 in an ``Xattention.py`` file of the codewithpapers function list.  They print
 none of its steps.  This module writes out the published method as read here
-(every point is a reading, listed in the design notes as x1..x7):
+(every point is a reading of the pages, labelled x1..x7):
 
   x1  block size B and stride S with B % S == 0; R = B / S reshaped rows per block.
   x2  reshaped rows: query row a stands for positions a*S + (S-1-s), key row b

@@ -7,7 +7,7 @@ come from a seeded ``torch.Generator`` on the GPU.  bf16 values are produced
 from fp32 by round-to-nearest-even and carried on the host as their uint16 bit
 patterns.
 
-Workload shapes follow the task's configurations: Llama-3.1-8B attention
+Workload shapes: Llama-3.1-8B attention
 (32 query heads, 8 KV heads, head_dim 128) and Qwen3-4B attention (same head
 layout, 36 layers, hidden 2560), the model shapes the pages evaluate on
 [thelatestinai paper page, Tables 1, 15, 18].
