@@ -1,0 +1,81 @@
+"""Full-size parity in the benchmark's own launch configuration: the router on
+the benchmark's 131072 x 4096 input and seeds, and the FA and SA prefill layers
+at 131072 tokens through the kernels the benchmark launches (picked from the
+host copy of the route), on sampled rows the oracle computes one by one."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_layerrouter_amd import _lib, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+T = 131072
+HIDDEN, ROUTER_HIDDEN, N_LAYERS, POOL = 4096, 256, 32, 64
+SINK, WINDOW, BLOCK = 128, 2048, 64
+
+
+def host_bf16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def test_router_on_the_benchmark_input():
+    """x_Q [131072, 4096] bf16 (seed 11), Xavier 4096 -> 256 -> 32 (rng seed 0): the
+    route bits bit-exact and the logits within fp32 rounding of the oracle, which
+    pools the same last 64 rows."""
+    x = synth.device_normal((T, HIDDEN), seed=11)
+    rng = np.random.default_rng(0)
+    w1, b1, w2, b2 = synth.router_weights(rng, HIDDEN, ROUTER_HIDDEN, N_LAYERS)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=DEV)
+    route = torch.zeros((1, N_LAYERS), dtype=torch.uint8, device=DEV)
+    logits = torch.zeros((1, N_LAYERS), dtype=torch.float32, device=DEV)
+    ws = torch.empty(_lib.fa_router_workspace_size(1, HIDDEN, ROUTER_HIDDEN), dtype=torch.uint8,
+                     device=DEV)
+    wd = [torch.from_numpy(a).to(DEV) for a in (w1, b1, w2, b2)]
+    _lib.fa_router_decide(x, cu, POOL, *wd, route, logits, ws)
+    torch.cuda.synchronize()
+    tail = host_bf16(x[T - POOL:])  # the pooling window: the last 64 rows
+    r_ref, _, l64 = oracle.router(tail, np.array([0, POOL], np.int32), POOL, w1, b1, w2, b2)
+    assert np.abs(l64).min() > 1e-4, "a logit sits on the threshold: bit not determined"
+    assert np.array_equal(route.cpu().numpy(), r_ref)
+    assert np.abs(logits.cpu().numpy() - l64).max() < 1e-5
+
+
+def sample_rows(n_random, seed, fa):
+    rng = np.random.default_rng(seed)
+    if fa:  # the FA oracle costs O(T) per row: a few rows at each end and at random
+        rows = {0, 1, 63, 64, 2047, 2048, T - 65, T - 64, T - 2, T - 1}
+    else:
+        rows = set(range(64)) | set(range(T - 64, T))
+        for edge in (SINK, WINDOW, SINK + WINDOW):
+            rows |= {edge - 1, edge, edge + 1}
+    rows |= set(rng.integers(0, T, n_random).tolist())
+    return np.array(sorted(rows), np.int32)
+
+
+@pytest.mark.parametrize("bit", [1, 0])
+def test_prefill_131k_sampled_rows(bit):
+    """One Llama-shaped layer (32 q / 8 kv heads, d 128, bf16) at 131072 tokens, run
+    as FA and as SA (sink 128, window 2048, block 64) with the host route copy, so
+    the per-kind kernel the benchmark times runs; every head of sampled rows."""
+    hq, hkv, d = 32, 8, 128
+    q = synth.device_normal((T, hq, d), seed=100)
+    k = synth.device_normal((T, hkv, d), seed=101)
+    v = synth.device_normal((T, hkv, d), seed=102)
+    o = torch.empty_like(q)
+    lse = torch.empty((T, hq), dtype=torch.float32, device=DEV)
+    r = np.array([[bit]], np.uint8)
+    scale = 1 / math.sqrt(d)
+    _lib.fa_attn_prefill(q, k, v, o, torch.tensor([0, T], dtype=torch.int32, device=DEV), T,
+                         torch.tensor(r, device=DEV), 0, SINK, WINDOW, BLOCK, scale, lse=lse,
+                         route_host=r)
+    torch.cuda.synchronize()
+    rows = sample_rows(4 if bit else 200, seed=7 + bit, fa=bool(bit))
+    o_ref, l_ref = oracle.attn_prefill(host_bf16(q), host_bf16(k), host_bf16(v), [0, T], r, 0,
+                                       SINK, WINDOW, BLOCK, scale, rows=rows)
+    got = synth.bf16_bits_to_f32(host_bf16(o)[rows]).astype(np.float64)
+    assert np.abs(got - o_ref).max() <= 2e-2
+    assert np.abs(lse.cpu().numpy()[rows] - l_ref).max() <= 1e-3
