@@ -79,3 +79,34 @@ def test_prefill_131k_sampled_rows(bit):
     got = synth.bf16_bits_to_f32(host_bf16(o)[rows]).astype(np.float64)
     assert np.abs(got - o_ref).max() <= 2e-2
     assert np.abs(lse.cpu().numpy()[rows] - l_ref).max() <= 1e-3
+
+
+@pytest.mark.parametrize("bs", [32])
+def test_decode_serving_batch_32k_sampled_heads(bs):
+    """The batched-serving launch: batch 32 over 32768-token bf16 caches (Llama shape),
+    the route copy on the host, one FA and one SA layer; KV heads 0 and 7 of every
+    sequence against the oracle."""
+    hq, hkv, d, n = 32, 8, 128, 32768
+    G = hq // hkv
+    kc = torch.empty((bs, hkv, n, d), dtype=torch.bfloat16, device=DEV)
+    vc = torch.empty_like(kc)
+    for b in range(bs):
+        kc[b] = synth.device_normal((hkv, n, d), seed=500 + b)
+        vc[b] = synth.device_normal((hkv, n, d), seed=600 + b)
+    q = synth.device_normal((bs, hq, d), seed=700)
+    cl = torch.full((bs,), n, dtype=torch.int32, device=DEV)
+    r = np.array([[1, 0]] * bs, np.uint8)
+    scale = 1 / math.sqrt(d)
+    for layer in (0, 1):
+        o = torch.empty_like(q)
+        lse = torch.empty((bs, hq), dtype=torch.float32, device=DEV)
+        _lib.fa_attn_decode(q, o, kc, vc, cl, torch.tensor(r, device=DEV), layer, SINK, WINDOW,
+                            BLOCK, scale, lse=lse, route_host=r)
+        torch.cuda.synchronize()
+        for g in (0, hkv - 1):
+            o_ref, l_ref = oracle.attn_decode(
+                host_bf16(q[:, g * G:(g + 1) * G]), host_bf16(kc[:, g:g + 1]),
+                host_bf16(vc[:, g:g + 1]), [n] * bs, r, layer, SINK, WINDOW, BLOCK, scale)
+            og = synth.bf16_bits_to_f32(host_bf16(o[:, g * G:(g + 1) * G])).astype(np.float64)
+            assert np.abs(og - o_ref).max() <= 2e-2
+            assert np.abs(lse[:, g * G:(g + 1) * G].cpu().numpy() - l_ref).max() <= 1e-3
