@@ -473,7 +473,9 @@ def main():
         nwx = -(-nqb // 32)
         sc = torch.empty((1, HQ, nqb, nqb), dtype=torch.float32, device=dev)
         mk = torch.empty((1, HQ, nqb, nwx), dtype=torch.int32, device=dev)
-        xa_flop = 2 * HQ * (nqb * (nqb + 1) // 2) * 16 * 16 * (XS * D) * 2  # two passes
+        xw = torch.empty(_lib.fa_xattn_workspace_size(1, HQ, nqb), dtype=torch.uint8,
+                         device=dev)
+        xa_flop = HQ * (nqb * (nqb + 1) // 2) * 16 * 16 * (XS * D) * 2
         xattn = {"block": XB, "stride": XS, "threshold": XTAU, "seq": T,
                  "fa_layer_ms": round(t_fa * 1e3, 3),
                  "sa_layer_ms": round(t_sa * 1e3, 3) if sa_layers else None,
@@ -487,7 +489,7 @@ def main():
             for rep in range(2):  # first run warms up, second is timed
                 e = [ev() for _ in range(4)]
                 e[0].record(stream)
-                _lib.fa_xattn_scores(q, k, cu, T, XB, XS, scale, sc)
+                _lib.fa_xattn_scores(q, k, cu, T, XB, XS, scale, sc, xw)
                 e[1].record(stream)
                 _lib.fa_xattn_select(sc, cu, XB, XTAU, mk)
                 e[2].record(stream)
@@ -505,7 +507,7 @@ def main():
                 "speedup_vs_fa_layer": round(t_fa * 1e3 / layer, 3),
                 "scores_tflops": round(xa_flop / (t3[0] * 1e-3) / 1e12, 1)}
             del q, k, v
-        del sc, mk
+        del sc, mk, xw
         log("xattn branch done")
 
     # ---- Triangle Attention as the sparse branch of one layer at T: the streaming

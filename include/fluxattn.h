@@ -258,19 +258,32 @@ fa_status fa_attn_prefill_triangle(const void *q, const void *k, const void *v,
  * scores [batch][n_q_heads][n_qblocks][n_qblocks] fp32 out; entries with
  *   j > i or past a sequence's blocks are not written.
  * n_qblocks >= ceil(max_seqlen / block_tokens), <= 4096 (layout of scores).
+ * workspace: device scratch of at least fa_xattn_workspace_size(batch,
+ *   n_q_heads, n_qblocks) bytes (each reshaped row's partial sums of every
+ *   key block, rescaled by a second kernel); caller-owned, contents undefined
+ *   on return.
  * Supported: bf16, head_dim 64 or 128, stride 4 or 8 with block = 16 * stride,
  * G in {1, 2, 4, 8, 16}.  Fixed reduction orders: repeated calls are bitwise
  * identical.
  * Errors: NULL pointer, batch/max_seqlen <= 0, bad heads, sm_scale not finite
  * or <= 0, block != 16 * stride, n_qblocks out of range -> FA_ERR_INVALID_ARG;
- * other dtype / head_dim / stride / G -> FA_ERR_UNSUPPORTED.
+ * workspace NULL or too small -> FA_ERR_WORKSPACE; other dtype / head_dim /
+ * stride / G -> FA_ERR_UNSUPPORTED.
  */
 fa_status fa_xattn_scores(const void *q, const void *k, int32_t dtype,
                           const int32_t *cu_seqlens, int32_t batch,
                           int32_t max_seqlen, int32_t n_q_heads,
                           int32_t n_kv_heads, int32_t head_dim,
                           int32_t block_tokens, int32_t stride, float sm_scale,
-                          float *scores, int32_t n_qblocks, void *stream);
+                          float *scores, int32_t n_qblocks, void *workspace,
+                          size_t ws_bytes, void *stream);
+
+/* Bytes of workspace fa_xattn_scores needs: 128 bytes per (sequence, head, cell
+ * j <= i) plus 128 per (sequence, head, query block), rounded up to 256; 0 for
+ * non-positive sizes or n_qblocks > 4096.  About 2.2 GB for 32 heads of one
+ * 131072-token sequence at block 128. */
+size_t fa_xattn_workspace_size(int32_t batch, int32_t n_q_heads,
+                               int32_t n_qblocks);
 
 /*
  * fa_xattn_select -- kept blocks per (sequence, head, query block i): block 0

@@ -9,6 +9,6 @@ from ._lib import (  # noqa: F401
     FA_OK, FluxAttnError, fa_abi_version, fa_attn_decode, fa_attn_prefill, fa_block_plan,
     fa_attn_decode_ring, fa_attn_prefill_kv, fa_decode_workspace_size, fa_kv_compact,
     fa_router_decide, fa_xattn_scores, fa_xattn_select, fa_attn_prefill_xattn,
-    fa_attn_prefill_triangle,
+    fa_attn_prefill_triangle, fa_xattn_workspace_size,
     fa_router_workspace_size, last_error, lib,
 )

@@ -24,6 +24,7 @@ EXPORTS = (
     "fa_block_plan", "fa_attn_prefill", "fa_decode_workspace_size", "fa_attn_decode",
     "fa_kv_compact", "fa_attn_decode_ring", "fa_attn_prefill_kv", "fa_xattn_scores",
     "fa_xattn_select", "fa_attn_prefill_xattn", "fa_attn_prefill_triangle",
+    "fa_xattn_workspace_size",
 )
 
 
@@ -66,7 +67,10 @@ def lib() -> ctypes.CDLL:
     L.fa_attn_prefill_triangle.argtypes = [P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, P, P,
                                            I32, I32, I32, I32, I32, I32, F, P]
     L.fa_xattn_scores.restype = I32
-    L.fa_xattn_scores.argtypes = [P, P, I32, P, I32, I32, I32, I32, I32, I32, I32, F, P, I32, P]
+    L.fa_xattn_scores.argtypes = [P, P, I32, P, I32, I32, I32, I32, I32, I32, I32, F, P, I32, P,
+                                  SZ, P]
+    L.fa_xattn_workspace_size.restype = SZ
+    L.fa_xattn_workspace_size.argtypes = [I32, I32, I32]
     L.fa_xattn_select.restype = I32
     L.fa_xattn_select.argtypes = [P, P, I32, I32, I32, I32, F, P, P]
     L.fa_attn_prefill_xattn.restype = I32
@@ -230,16 +234,25 @@ def fa_attn_prefill_triangle(q, k, v, o, cu_seqlens, max_seqlen, route, layer, s
     del keep
 
 
+def fa_xattn_workspace_size(batch, n_q_heads, n_qblocks) -> int:
+    return int(lib().fa_xattn_workspace_size(batch, n_q_heads, n_qblocks))
+
+
 def fa_xattn_scores(q, k, cu_seqlens, max_seqlen, block_tokens, stride, sm_scale, scores,
-                    stream=None):
+                    workspace=None, stream=None):
     """XAttention antidiagonal block scores: scores [B, Hq, NQB, NQB] float32 out."""
-    _require_cuda(q, k, cu_seqlens, scores)
+    import torch
+    _require_cuda(q, k, cu_seqlens, scores, workspace)
     batch = cu_seqlens.numel() - 1
     _, hq, d = q.shape
+    nqb = scores.shape[2]
+    if workspace is None:
+        n = fa_xattn_workspace_size(batch, hq, nqb)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
     _check(lib().fa_xattn_scores(
         _ptr(q), _ptr(k), _dtype_code(q), _ptr(cu_seqlens), batch, int(max_seqlen), hq,
-        k.shape[1], d, block_tokens, stride, float(sm_scale), _ptr(scores), scores.shape[2],
-        _stream(stream)))
+        k.shape[1], d, block_tokens, stride, float(sm_scale), _ptr(scores), nqb,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def fa_xattn_select(scores, cu_seqlens, block_tokens, threshold, mask, stream=None):

@@ -143,7 +143,7 @@ extern "C" {
 
 const char *fa_last_error(void) { return g_last_error.c_str(); }
 
-int32_t fa_abi_version(void) { return 6; }
+int32_t fa_abi_version(void) { return 7; }
 
 size_t fa_router_workspace_size(int32_t batch, int32_t hidden, int32_t router_hidden)
 {
@@ -263,11 +263,17 @@ fa_status fa_attn_prefill_kv(const void *q, const void *k, const void *v, void *
                         stream);
 }
 
+size_t fa_xattn_workspace_size(int32_t batch, int32_t n_q_heads, int32_t n_qblocks)
+{
+    if (batch <= 0 || n_q_heads <= 0 || n_qblocks <= 0 || n_qblocks > 4096) return 0;
+    return round256(fa::xa_scores_workspace_bytes(batch, n_q_heads, n_qblocks));
+}
+
 fa_status fa_xattn_scores(const void *q, const void *k, int32_t dtype,
                           const int32_t *cu_seqlens, int32_t batch, int32_t max_seqlen,
                           int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                           int32_t block_tokens, int32_t stride, float sm_scale, float *scores,
-                          int32_t n_qblocks, void *stream)
+                          int32_t n_qblocks, void *workspace, size_t ws_bytes, void *stream)
 {
     const char *fn = "fa_xattn_scores";
     if (!q || !k || !cu_seqlens || !scores)
@@ -297,7 +303,12 @@ fa_status fa_xattn_scores(const void *q, const void *k, int32_t dtype,
     const int G = n_q_heads / n_kv_heads;
     if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
         return fail(FA_ERR_UNSUPPORTED, "%s: GQA ratio %d not in {1,2,4,8,16}", fn, G);
+    const size_t ws_need = fa_xattn_workspace_size(batch, n_q_heads, n_qblocks);
+    if (!workspace || ws_bytes < ws_need)
+        return fail(FA_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn,
+                    workspace ? ws_bytes : (size_t)0, ws_need);
     fa::XaScoreArgs a{};
+    a.workspace = workspace;
     a.q = q;
     a.k = k;
     a.cu_seqlens = cu_seqlens;

@@ -106,7 +106,9 @@ struct XaScoreArgs {
     int nqb;                        // query blocks per sequence in the score layout
     float sm_scale;
     float *scores;                  // [batch][hq][nqb][nqb]
+    void *workspace;                // xa_scores_workspace_bytes(batch, hq, nqb)
 };
+size_t xa_scores_workspace_bytes(int batch, int hq, int nqb);
 hipError_t launch_xa_scores(const XaScoreArgs &a, hipStream_t stream);
 
 struct XaSelectArgs {

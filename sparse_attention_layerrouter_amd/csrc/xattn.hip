@@ -24,8 +24,11 @@
 // straight from global memory into LDS (buffer loads with an LDS destination,
 // three buffers, two tiles ahead) once for all 8 waves and read as the A
 // operand, 8 reads in flight ahead of the matrix core.  Two passes over the key
-// blocks: the first finds every reshaped row's log-sum-exp, the second sums
-// 2^(A - lse) per key block.  No workspace; fixed reduction orders.
+// blocks would redo every product; instead one pass keeps each reshaped row's
+// running max and sum and stores the row's sum over every key block with the
+// max it is relative to (a workspace of 8 bytes per row and cell), and a small
+// kernel rescales those to the row's log-sum-exp and adds the 16 rows of each
+// block.  Fixed reduction orders throughout.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -38,6 +41,13 @@ constexpr int kXaMaxBlocks = 4096;
 constexpr int kXaRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kXaLook = 8;                // LDS operand reads in flight
 constexpr int kXaWaves = 8;
+
+// row partials of the single score pass: one (sum, max) pair per reshaped row of
+// every cell j <= i of every (sequence, head), cells of row i at i (i+1) / 2
+__host__ __device__ inline size_t xa_part_entries(int batch, int hq, int nqb)
+{
+    return (size_t)batch * hq * ((size_t)nqb * (nqb + 1) / 2) * kXaRows;
+}
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c)
 {
@@ -108,7 +118,7 @@ template <int D, int S>
 __global__ __launch_bounds__(kXaWaves * 64) void xa_score_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const int32_t *__restrict__ cu,
     int hq, int hkv, int G, int hpw, int n_hgroups, int n_units, int npairs, int nqb,
-    float scale_log2, float *__restrict__ scores)
+    float scale_log2, float2 *__restrict__ part, float2 *__restrict__ rowstat)
 {
     constexpr int B = kXaRows * S;   // positions per block
     constexpr int NK = S * D / 32;   // k-steps of one reshaped row
@@ -230,14 +240,27 @@ __global__ __launch_bounds__(kXaWaves * 64) void xa_score_kernel(
         return (acc[0] + acc[1]) + (acc[2] + acc[3]);
     };
 
-    float m_l = -INFINITY, l_l = 0.0f, lse_row = 0.0f;
-    // pass 1: the score of key block j is kept by lane j % 64 and stored 64 at
-    // a time, so no store sits between a tile's copies and the wait for them
-    float stash = 0.0f;
-    float *srow = scores + (((size_t)b * hq + h) * nqb + i) * nqb;
+    // One pass.  Per reshaped row (held by lanes l, l^16, l^32, l^48): the
+    // running max m and the sum l of 2^(A - m) over the blocks so far; after
+    // block j the row's sum over that block, relative to the running max then,
+    // goes to the workspace with that max.  The finishing kernel rescales to the
+    // row's log-sum-exp and adds the 16 rows of each block.  A row's results of
+    // block j are stored at the start of the next block, before its tile
+    // copies, so the tile waits count copies only.
+    float m_row = -INFINITY, l_row = 0.0f;
+    float e_out = 0.0f, m_out = -INFINITY;  // the pending store
+    int j_out = -1;
+    const size_t ncell = (size_t)nqb * (nqb + 1) / 2;  // cells j <= i of one (b, h)
+    float2 *pbase = part + (((size_t)b * hq + h) * ncell + (size_t)i * (i + 1) / 2) * kXaRows;
+    auto flush = [&]() __attribute__((always_inline)) {
+        if (j_out >= 0 && active && kq == 0)  // uniform but for kq: lanes 0..15, one row each
+            pbase[(size_t)j_out * kXaRows + a_loc] = make_float2(e_out, m_out);
+        j_out = -1;
+    };
     // one key block j (tile in t); C lane layout: query row a = 16 i + l%16,
     // key columns 16 j + 4 (l/16) + jj
-    auto step = [&](auto pass, int j, const char *t) __attribute__((always_inline)) {
+    auto step = [&](int j, const char *t) __attribute__((always_inline)) {
+        flush();
         if (j > i) return;  // uniform: past the causal edge of this wave's block
         const f32x4 c = block_product(t);
         float v[4];
@@ -248,60 +271,78 @@ __global__ __launch_bounds__(kXaWaves * 64) void xa_score_kernel(
             ok[jj] = cb <= a && a < Tr;
             v[jj] = c[jj] * scale_log2;
         }
-        if constexpr (decltype(pass)::value == 0) {
-            // running max / sum (log2 domain) over the lane's values
-            float mb = -INFINITY;
+        float mb = fmaxf(fmaxf(ok[0] ? v[0] : -INFINITY, ok[1] ? v[1] : -INFINITY),
+                         fmaxf(ok[2] ? v[2] : -INFINITY, ok[3] ? v[3] : -INFINITY));
+        mb = row4_max(mb);
+        const float m_new = fmaxf(m_row, mb);
+        const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
+        float e = 0.0f;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) mb = ok[jj] ? fmaxf(mb, v[jj]) : mb;
-            const float m_new = fmaxf(m_l, mb);
-            if (m_new != -INFINITY) {
-                float l = l_l * fast_exp2(m_l - m_new);
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) l += ok[jj] ? fast_exp2(v[jj] - m_new) : 0.0f;
-                l_l = l;
-                m_l = m_new;
-            }
-        } else {
-            float e_sum = 0.0f;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) e_sum += ok[jj] ? fast_exp2(v[jj] - lse_row) : 0.0f;
-            e_sum = group_sum<32>(e_sum);
-            e_sum = sum_xor32(e_sum);
-            const int slot = j & 63;
-            if (lane == slot) stash = e_sum;
-            if (slot == 63 || j == i) {  // uniform
-                if (active && lane <= slot) srow[(j & ~63) + lane] = stash;
-            }
-        }
-    };
-    auto run_pass = [&](auto pass) __attribute__((always_inline)) {
-        issue_tile(0, lds0);
-        issue_tile(1, lds1);
-        tile_ready(0, lds0);
-        for (int j = 0; j <= j_last; j += 3) {
-            issue_tile(j + 2, lds2);
-            step(pass, j, lds0);
-            tile_ready(j + 1, lds1);
-            if (j + 1 > j_last) break;
-            issue_tile(j + 3, lds0);
-            step(pass, j + 1, lds1);
-            tile_ready(j + 2, lds2);
-            if (j + 2 > j_last) break;
-            issue_tile(j + 4, lds1);
-            step(pass, j + 2, lds2);
-            tile_ready(j + 3, lds0);
-        }
-        // drain the copies of tiles past the end before the buffers are reused
-        vm_wait_barrier(ic<0>{});
+        for (int jj = 0; jj < 4; ++jj) e += ok[jj] ? fast_exp2(v[jj] - m_sub) : 0.0f;
+        e = row4_sum(e);
+        l_row = l_row * fast_exp2(m_row - m_sub) + e;
+        m_row = m_new;
+        e_out = e;
+        m_out = m_new;
+        j_out = j;
     };
 
-    run_pass(ic<0>{});
-    {
-        const float M = row4_max(m_l);
-        const float L = row4_sum(m_l == -INFINITY ? 0.0f : l_l * fast_exp2(m_l - M));
-        lse_row = M + fast_log2(L);
+    // resolve the scalar kernel arguments the loop uses now: a scalar load still
+    // in flight inside the loop would turn every LDS wait there into lgkmcnt(0)
+    asm volatile("" ::"s"(pbase), "s"(scale_log2));
+    issue_tile(0, lds0);
+    issue_tile(1, lds1);
+    tile_ready(0, lds0);
+    for (int j = 0; j <= j_last; j += 3) {
+        issue_tile(j + 2, lds2);
+        step(j, lds0);
+        tile_ready(j + 1, lds1);
+        if (j + 1 > j_last) break;
+        issue_tile(j + 3, lds0);
+        step(j + 1, lds1);
+        tile_ready(j + 2, lds2);
+        if (j + 2 > j_last) break;
+        issue_tile(j + 4, lds1);
+        step(j + 2, lds2);
+        tile_ready(j + 3, lds0);
     }
-    run_pass(ic<1>{});
+    flush();
+    // the row's max and sum (2^lse = l 2^m); rows past the sequence end have l = 0
+    if (active && kq == 0)
+        rowstat[(((size_t)b * hq + h) * nqb + i) * kXaRows + a_loc] = make_float2(m_row, l_row);
+    // drain the copies of tiles past the end before the workgroup leaves
+    vm_wait_barrier(ic<0>{});
+}
+
+// Block scores from the row partials: score[i][j] = sum over the 16 rows r of
+// block i (ascending) of e_rj 2^(m_rj - M_r) / l_r, rows with l_r = 0 (past the
+// sequence end) left out.  One workgroup per (query block i, head, sequence).
+__global__ __launch_bounds__(256) void xa_score_finish_kernel(
+    const float2 *__restrict__ part, const float2 *__restrict__ rowstat,
+    const int32_t *__restrict__ cu, int hq, int nqb, int block, float *__restrict__ scores)
+{
+    const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int T = cu[b + 1] - cu[b];
+    const int nb = T > 0 ? (T + block - 1) / block : 0;
+    if (i >= nb) return;
+    __shared__ float2 st[kXaRows];
+    if (threadIdx.x < kXaRows)
+        st[threadIdx.x] = rowstat[(((size_t)b * hq + h) * nqb + i) * kXaRows + threadIdx.x];
+    __syncthreads();
+    const size_t ncell = (size_t)nqb * (nqb + 1) / 2;
+    const float2 *pb = part + (((size_t)b * hq + h) * ncell + (size_t)i * (i + 1) / 2) * kXaRows;
+    float *srow = scores + (((size_t)b * hq + h) * nqb + i) * nqb;
+    for (int j = threadIdx.x; j <= i; j += blockDim.x) {
+        const float2 *pc = pb + (size_t)j * kXaRows;
+        float sum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < kXaRows; ++r) {
+            const float2 em = pc[r];
+            const float2 ml = st[r];
+            if (ml.y > 0.0f) sum += em.x * fast_exp2(em.y - ml.x) / ml.y;
+        }
+        srow[j] = sum;
+    }
 }
 
 // One workgroup per (query block i, head h, sequence b): the kept-block bits.
@@ -384,13 +425,25 @@ hipError_t launch_scores_t(const XaScoreArgs &a, hipStream_t stream)
     const int npairs = (a.nqb + 1) / 2;
     const long long n_wg = (long long)npairs * n_hgroups * n_units;
     if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    float2 *part = (float2 *)a.workspace;
+    float2 *rowstat = part + xa_part_entries(a.batch, a.hq, a.nqb);
     xa_score_kernel<D, S><<<(unsigned)n_wg, kXaWaves * 64, 0, stream>>>(
         (const uint16_t *)a.q, (const uint16_t *)a.k, a.cu_seqlens, a.hq, a.hkv, G, hpw,
-        n_hgroups, n_units, npairs, a.nqb, a.sm_scale / S * kLog2e, a.scores);
+        n_hgroups, n_units, npairs, a.nqb, a.sm_scale / S * kLog2e, part, rowstat);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 grid(a.nqb, a.hq, a.batch);
+    xa_score_finish_kernel<<<grid, 256, 0, stream>>>(part, rowstat, a.cu_seqlens, a.hq, a.nqb,
+                                                     kXaRows * S, a.scores);
     return hipGetLastError();
 }
 
 }  // namespace
+
+size_t xa_scores_workspace_bytes(int batch, int hq, int nqb)
+{
+    return (xa_part_entries(batch, hq, nqb) + (size_t)batch * hq * nqb * kXaRows) * sizeof(float2);
+}
 
 hipError_t launch_xa_scores(const XaScoreArgs &a, hipStream_t stream)
 {

@@ -27,14 +27,14 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     assert set(names) == set(_lib.EXPORTS)
     for name in names:
         assert hasattr(L, name), name
 
 
 def test_abi_version_and_clean_error_state():
-    assert _lib.fa_abi_version() == 6
+    assert _lib.fa_abi_version() == 7
 
 
 def test_workspace_sizes():
@@ -233,3 +233,52 @@ def test_decode_ring_validation(kw, status):
                            "ws_bytes", "stream")]
     assert _lib.lib().fa_attn_decode_ring(*args) == status
     assert _lib.last_error().startswith("fa_attn_decode_ring")
+
+
+def test_xattn_workspace_size():
+    # 16 (max, sum) float2 pairs per (head, cell j <= i) plus 16 per (head, query block)
+    nqb = 1024
+    raw = (8 * 32 * (nqb * (nqb + 1) // 2) * 16 + 8 * 32 * nqb * 16) * 8
+    assert _lib.fa_xattn_workspace_size(8, 32, nqb) == (raw + 255) // 256 * 256
+    assert _lib.fa_xattn_workspace_size(1, 1, 1) == 256
+    assert _lib.fa_xattn_workspace_size(0, 32, 16) == 0
+    assert _lib.fa_xattn_workspace_size(1, 32, 4097) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), _lib.FA_ERR_INVALID_ARG),
+    (dict(scores=None), _lib.FA_ERR_INVALID_ARG),
+    (dict(batch=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(hq=30), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), _lib.FA_ERR_INVALID_ARG),
+    (dict(block=64), _lib.FA_ERR_INVALID_ARG),       # not 16 * stride
+    (dict(nqb=7), _lib.FA_ERR_INVALID_ARG),          # fewer than ceil(1000 / 128)
+    (dict(nqb=4097), _lib.FA_ERR_INVALID_ARG),
+    (dict(stride=2, block=32), _lib.FA_ERR_UNSUPPORTED),
+    (dict(dtype=0), _lib.FA_ERR_UNSUPPORTED),
+    (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
+    (dict(hq=24, hkv=8), _lib.FA_ERR_UNSUPPORTED),   # G = 3
+    (dict(ws=None), _lib.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), _lib.FA_ERR_WORKSPACE),
+])
+def test_xattn_scores_validation(kw, status):
+    a = dict(q=P, k=P, dtype=1, cu=P, batch=1, max_seqlen=1000, hq=32, hkv=8, d=128, block=128,
+             stride=8, scale=0.088, scores=P, nqb=8, ws=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    args = [a[k] for k in ("q", "k", "dtype", "cu", "batch", "max_seqlen", "hq", "hkv", "d",
+                           "block", "stride", "scale", "scores", "nqb", "ws", "ws_bytes",
+                           "stream")]
+    assert _lib.lib().fa_xattn_scores(*args) == status
+    assert _lib.last_error().startswith("fa_xattn_scores")
+
+
+@pytest.mark.parametrize("kw", [dict(scores=None), dict(batch=0), dict(nqb=0), dict(nqb=4097),
+                                dict(threshold=0.0), dict(threshold=float("nan"))])
+def test_xattn_select_validation(kw):
+    a = dict(scores=P, cu=P, batch=1, hq=32, nqb=8, block=128, threshold=0.9, mask=P,
+             stream=None)
+    a.update(kw)
+    args = [a[k] for k in ("scores", "cu", "batch", "hq", "nqb", "block", "threshold", "mask",
+                           "stream")]
+    assert _lib.lib().fa_xattn_select(*args) == _lib.FA_ERR_INVALID_ARG
+    assert _lib.last_error().startswith("fa_xattn_select")
