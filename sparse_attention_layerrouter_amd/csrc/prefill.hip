@@ -160,8 +160,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     constexpr int TILE_BYTES = kBN * D * 2;
     constexpr bool XA = MODE == kModeXA;
     // XA: kept-block words of the workgroup's heads, their union as a block list
+    // (entry: block index | bit 16 + hh set when head hh keeps the block)
     __shared__ uint32_t xa_head[XA ? 4 : 1][XA ? 128 : 1];
-    __shared__ uint16_t xa_list[XA ? 4096 : 1];
+    __shared__ uint32_t xa_list[XA ? 4096 : 1];
     __shared__ int xa_pre[XA ? 129 : 1];
     // separate arrays per buffer: the compiler can then tell that reads of one
     // buffer never wait for the asynchronous copies into the other
@@ -253,11 +254,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         }
         __syncthreads();
         for (int w = tid; w < xa_nw; w += kThreads) {
-            uint32_t u = 0;
-            for (int hh = 0; hh < hpw; ++hh) u |= xa_head[hh][w];
+            uint32_t hw[4];
+#pragma unroll
+            for (int hh = 0; hh < 4; ++hh) hw[hh] = hh < hpw ? xa_head[hh][w] : 0u;
+            uint32_t u = (hw[0] | hw[1]) | (hw[2] | hw[3]);
             int o = xa_pre[w];
             while (u) {
-                xa_list[o++] = (uint16_t)(32 * w + __builtin_ctz(u));
+                const int bit = __builtin_ctz(u);
+                uint32_t e = (uint32_t)(32 * w + bit);
+#pragma unroll
+                for (int hh = 0; hh < 4; ++hh) e |= ((hw[hh] >> bit) & 1u) << (16 + hh);
+                xa_list[o++] = e;
                 u &= u - 1;
             }
         }
@@ -271,15 +278,42 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         const int tB1 = (p1 + kBN - 1) / kBN;
         n_tiles = nA + max(0, tB1 - tB0);
     }
-    auto tile_k0 = [&](int t) __attribute__((always_inline)) {
+    // XA: list entries xa_base .. xa_base+63 live in one VGPR, entry xa_base + l
+    // in lane l, so a tile's entry is a lane read: no LDS round trip, and no LDS
+    // wait, inside the tile pipeline.  xa_window(t0), at the top of each round
+    // of phases (right after its barrier, when no LDS read is in flight), moves
+    // the window, with one LDS read, when the entries of tiles t0 .. t0+2 (all
+    // the round looks up) leave it: once per 62 blocks as the tiles ascend.
+    // Tile indices are clamped to [0, n_tiles - 1], as every lookup is.
+    uint32_t xa_win = 0u;
+    int xa_base = 1 << 30;
+    auto xa_window = [&](int t0) __attribute__((always_inline)) {
+        const int sh = rule.bk_log2 - 6;  // kBN = 64 keys per tile
+        const int lo = max(min(t0, n_tiles - 1), 0) >> sh;
+        const int hi = max(min(t0 + 2, n_tiles - 1), 0) >> sh;
+        if (lo < xa_base || hi >= xa_base + 64) {  // uniform
+            xa_base = lo;
+            xa_win = xa_list[min(lo + lane, 4095)];
+        }
+    };
+    auto xa_entry = [&](int t) __attribute__((always_inline)) {
+        const int e = max(t, 0) >> (rule.bk_log2 - 6);
+        return (uint32_t)__builtin_amdgcn_readlane((int)xa_win, e - xa_base);
+    };
+    // first key of tile t; in mode XA from its list entry ent
+    auto tile_k0e = [&](int t, uint32_t ent) __attribute__((always_inline)) {
         if constexpr (XA) {
-            const int sh = rule.bk_log2 - 6;  // kBN = 64 keys per tile
-            const int blk = __builtin_amdgcn_readfirstlane((int)xa_list[t >> sh]);
-            return (blk << rule.bk_log2) + ((t & ((1 << sh) - 1)) << 6);
+            const int sh = rule.bk_log2 - 6;
+            return ((int)(ent & 0xffffu) << rule.bk_log2) + ((t & ((1 << sh) - 1)) << 6);
         } else {
             return (t < nA ? t : tB0 + (t - nA)) * kBN;
         }
     };
+    auto tile_k0 = [&](int t) __attribute__((always_inline)) {
+        if constexpr (XA) return tile_k0e(t, xa_entry(t));
+        else return tile_k0e(t, 0u);
+    };
+    if constexpr (XA) xa_window(0);
 
     const size_t row_stride = (size_t)hkv * D;
     const uint16_t *kb = k + ((size_t)start * hkv + kvh) * D;
@@ -321,12 +355,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int my_t = min(pw0 + l32, T - 1);  // query position of this lane's row
     const int my_win_lo = ((my_t >> rule.bk_log2) - rule.nw + 1) << rule.bk_log2;
     const bool my_dense = is_fa || my_t >= tail0;
-    // does any row of this wave see a key of the tile at k0?
-    auto wave_sees = [&](int k0) __attribute__((always_inline)) {
+    // does any row of this wave see a key of the tile at k0 (list entry ent)?
+    auto wave_sees = [&](int k0, uint32_t ent) __attribute__((always_inline)) {
         if constexpr (XA) {  // this wave's head kept the tile's block
-            const int blk = k0 >> rule.bk_log2;
-            return wave_active && k0 <= pw_last &&
-                   ((xa_head[wq / wph][blk >> 5] >> (blk & 31)) & 1u) != 0;
+            return wave_active && k0 <= pw_last && ((ent >> (16 + wq / wph)) & 1u) != 0;
         } else {
             return wave_active && k0 <= pw_last &&
                    (w_dense_any || k0 < sink_tok || k0 + kBN > win_lo_min);
@@ -371,6 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) pk[kb2][j] = 0u;
     bool s_live = false;      // s holds a tile this wave sees
+    int k0_live = 0;          // first key of the tile in s
 
     // ---- MFMA block of tile t: S^T = K Q^T of tile t, O^T += V^T P^T of tile t-1
     // Operand reads from LDS: the K operand of d step ks / key block kb2, and
@@ -415,11 +448,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         constexpr int NDT = D / 32;
         constexpr int NLD = lk.NI + lv.NI;
         static_assert(4 * NLD <= NM, "copies fit between the MFMAs");
-        s_live = t < n_tiles && wave_sees(tile_k0(t));
+        const int tc = min(t, n_tiles - 1);
+        const uint32_t ent = XA ? xa_entry(tc) : 0u;
+        const int k0_t = tile_k0e(tc, ent);
+        k0_live = k0_t;
+        s_live = t < n_tiles && wave_sees(k0_t, ent);
         __amdgpu_buffer_rsrc_t rk, rv;
         if constexpr (LD) {
             rk = lk.rsrc(kb, row_stride, tile_k0(min(t + 1, n_tiles - 1)), T);
-            rv = lv.rsrc(vb, row_stride, tile_k0(min(t, n_tiles - 1)), T);
+            rv = lv.rsrc(vb, row_stride, k0_t, T);
         }
         s[0] = f32x16{};
         s[1] = f32x16{};
@@ -465,7 +502,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                 for (int j = 0; j < 8; ++j) pk[kb2][j] = 0u;
             return;
         }
-        const int k0 = tile_k0(t);
+        const int k0 = k0_live;  // tile t's first key, from its MFMA block
         // mask (causal diagonal, window lower edge, sequence tail)
         const bool need_mask = (k0 + kBN - 1 > pw0) ||
                                (!w_dense_all && k0 < win_lo_max && k0 + kBN > sink_tok);
@@ -556,6 +593,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         for (int p = 0; p < n_phases; p += 4) {
             const int t0 = p >> 1;  // even tile index of this round
             sync_even();
+            if constexpr (XA) xa_window(t0);
             if (GRP == 0) block_mfma(ic<1>{}, k_lds0, v_lds1, t0, k_lds1, v_lds0);
             else if (p > 0) block_valu(t0 - 1);
             if (p + 1 >= n_phases) break;

@@ -54,16 +54,18 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// reductions over the 4 lanes l, l^16, l^32, l^48 that hold one reshaped row
+// reductions over the 4 lanes l, l^16, l^32, l^48 that hold one reshaped row;
+// the lane ^ 16 step is a VALU row swap (no LDS round trip): with both operands
+// x, each lane receives x[l] and x[l ^ 16] in its two results
 __device__ __forceinline__ float row4_sum(float x)
 {
-    x += xor16(x);
-    return sum_xor32(x);
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return sum_xor32(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float row4_max(float x)
 {
-    x = fmaxf(x, xor16(x));
-    return max_xor32(x);
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return max_xor32(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
 }
 
 template <int V>
@@ -245,8 +247,7 @@ __global__ __launch_bounds__(kXaWaves * 64) void xa_score_kernel(
     // block j the row's sum over that block, relative to the running max then,
     // goes to the workspace with that max.  The finishing kernel rescales to the
     // row's log-sum-exp and adds the 16 rows of each block.  A row's results of
-    // block j are stored at the start of the next block, before its tile
-    // copies, so the tile waits count copies only.
+    // block j are stored before the next tile copies are issued.
     float m_row = -INFINITY, l_row = 0.0f;
     float e_out = 0.0f, m_out = -INFINITY;  // the pending store
     int j_out = -1;
@@ -257,12 +258,9 @@ __global__ __launch_bounds__(kXaWaves * 64) void xa_score_kernel(
             pbase[(size_t)j_out * kXaRows + a_loc] = make_float2(e_out, m_out);
         j_out = -1;
     };
-    // one key block j (tile in t); C lane layout: query row a = 16 i + l%16,
-    // key columns 16 j + 4 (l/16) + jj
-    auto step = [&](int j, const char *t) __attribute__((always_inline)) {
-        flush();
-        if (j > i) return;  // uniform: past the causal edge of this wave's block
-        const f32x4 c = block_product(t);
+    // softmax update with key block j's products c; C lane layout: query row
+    // a = 16 i + l%16, key columns 16 j + 4 (l/16) + jj
+    auto soft = [&](int j, const f32x4 &c) __attribute__((always_inline)) {
         float v[4];
         bool ok[4];
 #pragma unroll
@@ -286,6 +284,10 @@ __global__ __launch_bounds__(kXaWaves * 64) void xa_score_kernel(
         m_out = m_new;
         j_out = j;
     };
+    // one key block (tile in t)
+    auto step = [&](int j, const char *t) __attribute__((always_inline)) {
+        if (j <= i) soft(j, block_product(t));  // uniform: up to the causal edge
+    };
 
     // resolve the scalar kernel arguments the loop uses now: a scalar load still
     // in flight inside the loop would turn every LDS wait there into lgkmcnt(0)
@@ -294,14 +296,17 @@ __global__ __launch_bounds__(kXaWaves * 64) void xa_score_kernel(
     issue_tile(1, lds1);
     tile_ready(0, lds0);
     for (int j = 0; j <= j_last; j += 3) {
+        flush();
         issue_tile(j + 2, lds2);
         step(j, lds0);
         tile_ready(j + 1, lds1);
         if (j + 1 > j_last) break;
+        flush();
         issue_tile(j + 3, lds0);
         step(j + 1, lds1);
         tile_ready(j + 2, lds2);
         if (j + 2 > j_last) break;
+        flush();
         issue_tile(j + 4, lds1);
         step(j + 2, lds2);
         tile_ready(j + 3, lds0);
@@ -315,33 +320,42 @@ __global__ __launch_bounds__(kXaWaves * 64) void xa_score_kernel(
 }
 
 // Block scores from the row partials: score[i][j] = sum over the 16 rows r of
-// block i (ascending) of e_rj 2^(m_rj - M_r) / l_r, rows with l_r = 0 (past the
-// sequence end) left out.  One workgroup per (query block i, head, sequence).
+// block i of e_rj 2^(m_rj - M_r) / l_r, rows with l_r = 0 (past the sequence
+// end) left out.  One workgroup per (query block i, head, sequence); 8 lanes
+// per cell j, lane q reading rows 2q and 2q+1 (16 bytes, so a wave reads 1 KiB
+// in one coalesced load), summed over the 8 lanes in a fixed DPP order.
 __global__ __launch_bounds__(256) void xa_score_finish_kernel(
     const float2 *__restrict__ part, const float2 *__restrict__ rowstat,
     const int32_t *__restrict__ cu, int hq, int nqb, int block, float *__restrict__ scores)
 {
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
     const int T = cu[b + 1] - cu[b];
     const int nb = T > 0 ? (T + block - 1) / block : 0;
     if (i >= nb) return;
-    __shared__ float2 st[kXaRows];
-    if (threadIdx.x < kXaRows)
-        st[threadIdx.x] = rowstat[(((size_t)b * hq + h) * nqb + i) * kXaRows + threadIdx.x];
+    __shared__ float2 st[kXaRows];  // (M_r, 1 / l_r), 1 / l_r = 0 marking an empty row
+    if (tid < kXaRows) {
+        const float2 ml = rowstat[(((size_t)b * hq + h) * nqb + i) * kXaRows + tid];
+        st[tid] = make_float2(ml.x, ml.y > 0.0f ? 1.0f / ml.y : 0.0f);
+    }
     __syncthreads();
+    const int q = tid & 7;
+    const float2 s0 = st[2 * q], s1 = st[2 * q + 1];
     const size_t ncell = (size_t)nqb * (nqb + 1) / 2;
-    const float2 *pb = part + (((size_t)b * hq + h) * ncell + (size_t)i * (i + 1) / 2) * kXaRows;
+    const float4 *pb = (const float4 *)(part + (((size_t)b * hq + h) * ncell +
+                                                (size_t)i * (i + 1) / 2) * kXaRows);
     float *srow = scores + (((size_t)b * hq + h) * nqb + i) * nqb;
-    for (int j = threadIdx.x; j <= i; j += blockDim.x) {
-        const float2 *pc = pb + (size_t)j * kXaRows;
-        float sum = 0.0f;
-#pragma unroll
-        for (int r = 0; r < kXaRows; ++r) {
-            const float2 em = pc[r];
-            const float2 ml = st[r];
-            if (ml.y > 0.0f) sum += em.x * fast_exp2(em.y - ml.x) / ml.y;
+    for (int j0 = 0; j0 <= i; j0 += 32) {  // uniform: every lane joins the DPP sum
+        const int j = j0 + (tid >> 3);
+        float t = 0.0f;
+        if (j <= i) {
+            const float4 em = pb[(size_t)j * (kXaRows / 2) + q];
+            const float t0 = s0.y > 0.0f ? em.x * fast_exp2(em.y - s0.x) * s0.y : 0.0f;
+            const float t1 = s1.y > 0.0f ? em.z * fast_exp2(em.w - s1.x) * s1.y : 0.0f;
+            t = t0 + t1;
         }
-        srow[j] = sum;
+        t = group_sum<8>(t);
+        if (q == 0 && j <= i) srow[j] = t;
     }
 }
 
