@@ -125,33 +125,41 @@ def block_score_row(q_h, k_h, stride, sm_scale, block, i):
     return Pp.sum(axis=0).reshape(i + 1, R).sum(axis=1)
 
 
+def select_row(row32, i, threshold):
+    """x6 for query block i: row32 float32 scores score[i][0..i] (entries past i
+    are ignored) -> kept-block flags bool [i + 1]."""
+    row = np.asarray(row32, np.float32)
+    tau = np.float32(threshold)
+    keep = np.zeros(i + 1, bool)
+    total = np.float32(0.0)
+    for j in range(i + 1):
+        total = np.float32(total + row[j])
+    goal = np.float32(tau * total)
+    keep[0] = True
+    keep[i] = True
+    kept = np.float32(row[0])
+    if i > 0:
+        kept = np.float32(kept + row[i])
+    rest = sorted(range(1, i), key=lambda j: (-float(row[j]), j))
+    for j in rest:
+        if not kept < goal:
+            break
+        keep[j] = True
+        kept = np.float32(kept + row[j])
+    return keep
+
+
 def select_blocks(scores32, seqlens, block, threshold):
     """x6: scores float32 [B, H, NQB, NQB] (as the kernel produced them) ->
     kept-block mask bool [B, H, NQB, NQB]."""
     s = np.asarray(scores32, np.float32)
     B, H, nqb, _ = s.shape
-    tau = np.float32(threshold)
     keep = np.zeros(s.shape, bool)
     for b in range(B):
         nb = -(-int(seqlens[b]) // block)
         for h in range(H):
             for i in range(nb):
-                row = s[b, h, i]
-                total = np.float32(0.0)
-                for j in range(i + 1):
-                    total = np.float32(total + row[j])
-                goal = np.float32(tau * total)
-                keep[b, h, i, 0] = True
-                keep[b, h, i, i] = True
-                kept = np.float32(row[0])
-                if i > 0:
-                    kept = np.float32(kept + row[i])
-                rest = sorted(range(1, i), key=lambda j: (-float(row[j]), j))
-                for j in rest:
-                    if not kept < goal:
-                        break
-                    keep[b, h, i, j] = True
-                    kept = np.float32(kept + row[j])
+                keep[b, h, i, : i + 1] = select_row(s[b, h, i], i, threshold)
     return keep
 
 
