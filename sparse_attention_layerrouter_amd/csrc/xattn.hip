@@ -365,10 +365,12 @@ __global__ __launch_bounds__(256) void xa_select_kernel(const float *__restrict_
                                                         int nqb, int nw, int block, float tau,
                                                         uint32_t *__restrict__ mask)
 {
-    __shared__ float key_s[kXaMaxBlocks];
+    // 16 entries of padding: the decision loop loads 16 values at a time
+    __shared__ __attribute__((aligned(16))) float key_s[kXaMaxBlocks + 16];
     __shared__ int key_j[kXaMaxBlocks];
-    __shared__ float row_s[kXaMaxBlocks];
+    __shared__ __attribute__((aligned(16))) float row_s[kXaMaxBlocks + 16];
     __shared__ uint32_t bits[kXaMaxBlocks / 32];
+    __shared__ int s_cut;
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const int T = cu[b + 1] - cu[b];
@@ -410,20 +412,57 @@ __global__ __launch_bounds__(256) void xa_select_kernel(const float *__restrict_
             }
             __syncthreads();
         }
+    // The decision, on one lane: every sum is fp32, one add at a time in the
+    // stated order; the LDS loads fetch 16 values (4 x 16 bytes) ahead of the
+    // adds.  t0 < 4096 is a multiple of 16, so a chunk stays in the padded arrays;
+    // values past the row are loaded but never added.
     if (tid == 0) {
+        auto chunk = [&](const float *a, int t0, float (&x)[16]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float4 v = *(const float4 *)(a + t0 + 4 * u);
+                x[4 * u] = v.x;
+                x[4 * u + 1] = v.y;
+                x[4 * u + 2] = v.z;
+                x[4 * u + 3] = v.w;
+            }
+        };
+        float x[16];
         float total = 0.0f;
-        for (int j = 0; j <= i; ++j) total = total + row_s[j];
+        for (int t0 = 0; t0 <= i; t0 += 16) {
+            chunk(row_s, t0, x);
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (t0 + u <= i) total = total + x[u];
+        }
         const float goal = tau * total;
-        bits[0] |= 1u;
-        bits[i >> 5] |= 1u << (i & 31);
         float kept = row_s[0];
         if (i > 0) kept = kept + row_s[i];
-        for (int t = 0; t < n; ++t) {
-            if (!(kept < goal)) break;
-            const int j = key_j[t];
-            bits[j >> 5] |= 1u << (j & 31);
-            kept = kept + key_s[t];
+        // candidates in sorted order join while the kept sum is below the goal
+        int cut = 0;
+        bool stop = false;
+        for (int t0 = 0; t0 < n && !stop; t0 += 16) {
+            chunk(key_s, t0, x);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                if (stop || t0 + u >= n) break;
+                if (!(kept < goal)) {
+                    stop = true;
+                    break;
+                }
+                kept = kept + x[u];
+                cut = t0 + u + 1;
+            }
         }
+        s_cut = cut;
+        bits[0] |= 1u;
+        bits[i >> 5] |= 1u << (i & 31);
+    }
+    __syncthreads();
+    const int cut = s_cut;
+    for (int t = tid; t < cut; t += 256) {
+        const int j = key_j[t];
+        atomicOr(&bits[j >> 5], 1u << (j & 31));
     }
     __syncthreads();
     for (int w = tid; w < nw; w += 256) mrow[w] = bits[w];

@@ -179,6 +179,49 @@ def test_xattn_prefill_with_every_block_kept_is_the_fa_kernel(block):
     assert np.array_equal(lse, l_fa.cpu().numpy())
 
 
+def _tied_scores(rng, shape):
+    """fp32 score rows: half continuous, half from a few values (ties, zeros)."""
+    x = rng.random(shape, dtype=np.float32)
+    tied = rng.choice(np.array([0.0, 0.25, 1.0], np.float32), size=shape)
+    return np.where(rng.random(shape) < 0.5, tied, x).astype(np.float32)
+
+
+@pytest.mark.parametrize("tau", [0.3, 0.9, 0.999, 1.5])
+def test_selection_alone_matches_oracle_on_tied_scores(tau):
+    """fa_xattn_select on synthetic rows of up to 600 blocks (ragged sequences,
+    one of a single token): every row's kept bits equal the oracle's x6
+    decision on the same fp32 scores, ties broken by block index."""
+    rng = np.random.default_rng(int(tau * 1000))
+    block, nqb = 64, 600
+    lengths = [nqb * block - 17, 37 * block, 1]
+    nw = -(-nqb // 32)
+    sc = _tied_scores(rng, (len(lengths), 1, nqb, nqb))
+    m = torch.full((len(lengths), 1, nqb, nw), -1, dtype=torch.int32, device=DEV)
+    _lib.fa_xattn_select(dev_from(sc), torch.tensor(synth.cu_seqlens_of(lengths), device=DEV),
+                         block, tau, m)
+    torch.cuda.synchronize()
+    got = unpack(m.cpu().numpy(), nqb)
+    want = xattn.select_blocks(sc, lengths, block, tau)
+    assert np.array_equal(got, want)
+
+
+def test_selection_at_the_4096_block_maximum():
+    """Rows of a 4096-block sequence (the largest n_qblocks the ABI takes),
+    sampled where the decision's 16-value loads end at or past the last entry."""
+    rng = np.random.default_rng(4096)
+    block, nqb, tau = 16, 4096, 0.9
+    sc = _tied_scores(rng, (1, 1, nqb, nqb))
+    m = torch.full((1, 1, nqb, nqb // 32), -1, dtype=torch.int32, device=DEV)
+    _lib.fa_xattn_select(dev_from(sc), torch.tensor([0, nqb * block], device=DEV,
+                                                    dtype=torch.int32), block, tau, m)
+    torch.cuda.synchronize()
+    got = unpack(m.cpu().numpy(), nqb)
+    for i in [0, 1, 2, 15, 16, 17, 2047, 4079, 4080, 4081, 4094, 4095]:
+        want = xattn.select_row(sc[0, 0, i], i, tau)
+        assert np.array_equal(got[0, 0, i, : i + 1], want), i
+        assert not got[0, 0, i, i + 1:].any(), i
+
+
 def test_full_size_llama_128k_sampled():
     """A 131072-token Llama-shaped layer (32 q / 8 kv heads, d 128, bf16; block
     128, stride 8, threshold 0.9) on locality-structured inputs, launched as the
@@ -212,9 +255,7 @@ def test_full_size_llama_128k_sampled():
     for h, i in [(0, 0), (0, 1), (5, 300), (13, 511), (31, 1023), (22, 1022)]:
         ref = xattn.block_score_row(qh[:, h], kh[:, h // (hq // hkv)], stride, scale, block, i)
         assert np.abs(got[h, i, : i + 1] - ref).max() <= 1e-4, (h, i)
-        one = np.zeros((1, 1, i + 1, i + 1), np.float32)
-        one[0, 0, i] = got[h, i, : i + 1]
-        want = xattn.select_blocks(one, [(i + 1) * block], block, tau)[0, 0, i]
+        want = xattn.select_row(got[h, i], i, tau)
         assert np.array_equal(keep[0, h, i, : i + 1], want), (h, i)
         assert not keep[0, h, i, i + 1:].any(), (h, i)
     rows = [0, 127, 128, 65537, T - 1]
