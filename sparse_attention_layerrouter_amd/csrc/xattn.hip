@@ -231,8 +231,13 @@ __global__ __launch_bounds__(kXaWaves * 64) void xa_score_kernel(
             return __builtin_bit_cast(
                 bf16x8, *(const u32x4 *)(t + aoff[kk % NQ] + (kk * 32 / D) * (D * 2)));
         };
+        // reads issued in k order (LDS reads complete in issue order, so the
+        // first MFMA waits for the first read only)
 #pragma unroll
-        for (int kk = 0; kk < LK; ++kk) ab[kk] = rd(kk);
+        for (int kk = 0; kk < LK; ++kk) {
+            ab[kk] = rd(kk);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
             acc[kk & 3] = mfma16(ab[kk % LK], qr[kk], acc[kk & 3]);
@@ -289,9 +294,10 @@ __global__ __launch_bounds__(kXaWaves * 64) void xa_score_kernel(
         if (j <= i) soft(j, block_product(t));  // uniform: up to the causal edge
     };
 
-    // resolve the scalar kernel arguments the loop uses now: a scalar load still
-    // in flight inside the loop would turn every LDS wait there into lgkmcnt(0)
-    asm volatile("" ::"s"(pbase), "s"(scale_log2));
+    // resolve every scalar kernel argument the kernel still needs now, those
+    // used after the loop too: a scalar load still in flight at the loop
+    // header would turn the first LDS wait of every block into lgkmcnt(0)
+    asm volatile("" ::"s"(pbase), "s"(scale_log2), "s"(rowstat));
     issue_tile(0, lds0);
     issue_tile(1, lds1);
     tile_ready(0, lds0);
