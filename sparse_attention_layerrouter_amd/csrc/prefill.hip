@@ -755,12 +755,25 @@ hipError_t launch_generic(const PrefillArgs &a, hipStream_t stream, const Sparse
     return hipGetLastError();
 }
 
+// Query heads per workgroup: 4 (each K/V tile then serves 4 heads) unless the
+// model has fewer per KV head.  Mode XA needs the workgroup's 256 / hpw
+// positions inside one block, and walks the union of its heads' kept blocks:
+// it takes the fewest heads that fit (2 at block 128), so that union is over
+// fewer heads; 0 when none fits.
+int mfma_hpw(int G, int mode, int block)
+{
+    const int h = G >= 4 ? 4 : G;
+    if (mode != kModeXA) return h;
+    const int need = block >= 256 ? 1 : 256 / block;
+    return need <= h ? need : 0;
+}
+
 template <int D, int MODE>
 hipError_t launch_mfma(const PrefillArgs &a, hipStream_t stream, const SparseRule &r,
                        float scale_log2)
 {
     const int G = a.hq / a.hkv;
-    const int hpw = G >= 4 ? 4 : G;
+    const int hpw = mfma_hpw(G, MODE, 1 << a.bk_log2);
     const int n_hgroups = G / hpw;
     const int bm_pos = 2 * 32 * (4 / hpw);  // two groups of 4 waves x 32 rows
     const int n_ptiles = (a.max_seqlen + bm_pos - 1) / bm_pos;
@@ -784,10 +797,8 @@ hipError_t launch_mode(const PrefillArgs &a, hipStream_t stream, const SparseRul
                        float scale_log2)
 {
     const int G = a.hq / a.hkv;
-    // mode XA needs every workgroup's positions (2 groups x 32 x 4 / min(G, 4))
-    // inside one block
-    const bool xa_fits = MODE != kModeXA || 256 / (G >= 4 ? 4 : G) <= (1 << a.bk_log2);
-    if (a.bf16 && prefill_mfma_supported(a.d, G) && xa_fits) {
+    const bool fits = mfma_hpw(G, MODE, 1 << a.bk_log2) != 0;
+    if (a.bf16 && prefill_mfma_supported(a.d, G) && fits) {
         if (a.d == 128) return launch_mfma<128, MODE>(a, stream, r, scale_log2);
         return launch_mfma<64, MODE>(a, stream, r, scale_log2);
     }
