@@ -37,7 +37,6 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kXaRows = 16;  // reshaped rows (and columns) per block: B = 16 S
-constexpr int kXaMaxBlocks = 4096;
 constexpr int kXaRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kXaLook = 8;                // LDS operand reads in flight
 constexpr int kXaWaves = 8;
@@ -366,17 +365,26 @@ __global__ __launch_bounds__(256) void xa_score_finish_kernel(
 }
 
 // One workgroup per (query block i, head h, sequence b): the kept-block bits.
+// LDS of the selection kernel, sized per launch for Pm = max(16, the power of
+// two >= n_qblocks) so that more workgroups share a CU when rows are short:
+// key_s [Pm + 16] and row_s [Pm + 16] floats (16 entries of padding: the
+// decision loads 16 values at a time), key_j [Pm], bits [nw], the cut.
+__host__ __device__ inline size_t xa_select_lds_bytes(int pm, int nw)
+{
+    return (size_t)4 * (2 * (pm + 16) + pm + nw + 1);
+}
+
 __global__ __launch_bounds__(256) void xa_select_kernel(const float *__restrict__ scores,
                                                         const int32_t *__restrict__ cu, int hq,
-                                                        int nqb, int nw, int block, float tau,
-                                                        uint32_t *__restrict__ mask)
+                                                        int nqb, int nw, int pm, int block,
+                                                        float tau, uint32_t *__restrict__ mask)
 {
-    // 16 entries of padding: the decision loop loads 16 values at a time
-    __shared__ __attribute__((aligned(16))) float key_s[kXaMaxBlocks + 16];
-    __shared__ int key_j[kXaMaxBlocks];
-    __shared__ __attribute__((aligned(16))) float row_s[kXaMaxBlocks + 16];
-    __shared__ uint32_t bits[kXaMaxBlocks / 32];
-    __shared__ int s_cut;
+    extern __shared__ __attribute__((aligned(16))) float xa_sel_lds[];
+    float *key_s = xa_sel_lds;
+    float *row_s = key_s + pm + 16;  // 16-byte aligned: pm is a multiple of 16
+    int *key_j = (int *)(row_s + pm + 16);
+    uint32_t *bits = (uint32_t *)(key_j + pm);
+    int &s_cut = *(int *)(bits + nw);
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const int T = cu[b + 1] - cu[b];
@@ -420,8 +428,9 @@ __global__ __launch_bounds__(256) void xa_select_kernel(const float *__restrict_
         }
     // The decision, on one lane: every sum is fp32, one add at a time in the
     // stated order; the LDS loads fetch 16 values (4 x 16 bytes) ahead of the
-    // adds.  t0 < 4096 is a multiple of 16, so a chunk stays in the padded arrays;
-    // values past the row are loaded but never added.
+    // adds.  A chunk starts at a multiple of 16 below Pm (t0 <= i < n_qblocks,
+    // t0 < n <= Pm), so it stays in the padded arrays; values past the row are
+    // loaded but never added.
     if (tid == 0) {
         auto chunk = [&](const float *a, int t0, float (&x)[16]) __attribute__((always_inline)) {
 #pragma unroll
@@ -514,8 +523,10 @@ hipError_t launch_xa_scores(const XaScoreArgs &a, hipStream_t stream)
 hipError_t launch_xa_select(const XaSelectArgs &a, hipStream_t stream)
 {
     dim3 grid(a.nqb, a.hq, a.batch);
-    xa_select_kernel<<<grid, 256, 0, stream>>>(a.scores, a.cu_seqlens, a.hq, a.nqb, a.nw,
-                                               a.block, a.threshold, a.mask);
+    int pm = 16;
+    while (pm < a.nqb) pm <<= 1;
+    xa_select_kernel<<<grid, 256, xa_select_lds_bytes(pm, a.nw), stream>>>(
+        a.scores, a.cu_seqlens, a.hq, a.nqb, a.nw, pm, a.block, a.threshold, a.mask);
     return hipGetLastError();
 }
 
