@@ -50,6 +50,8 @@ CASES = [
     ([517], 4, 4, 128, 8),          # G = 1
     ([390, 200], 16, 2, 64, 8),     # G = 8, d = 64
     ([300], 4, 2, 64, 4),
+    ([600, 77], 4, 2, 128, 8),      # G = 2 at block 128: two heads per workgroup
+    ([260, 130], 16, 1, 128, 8),    # G = 16: eight head groups of two
 ]
 
 
@@ -126,6 +128,7 @@ XA_CASES = [
     ([390, 200], 16, 2, 64, 128, True, "random"),   # G = 8, d = 64
     ([300, 90], 8, 2, 128, 64, False, "random"),    # fp32: plain kernel
     ([600], 4, 2, 128, 128, True, "random"),        # G = 2, block 128: MFMA kernel
+    ([260, 130], 16, 1, 128, 128, True, "random"),  # G = 16: eight head groups of two
 ]
 
 
