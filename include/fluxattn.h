@@ -243,7 +243,7 @@ fa_status fa_attn_prefill_triangle(const void *q, const void *k, const void *v,
  * The pages name XAttention ("Block Sparse Attention with Antidiagonal
  * Scoring", mlsanity page reference list) as a block-level sparse operator for
  * prefill whose blocks are chosen by a selection score [thelatestinai paper
- * page, Table 4 and Table 12]; the branch runs in three calls:
+ * page, Table 3 and Table 12]; the branch runs in three calls:
  * fa_xattn_scores -> fa_xattn_select -> fa_attn_prefill_xattn.
  *
  * fa_xattn_scores -- antidiagonal block scores.  With stride S and block B =

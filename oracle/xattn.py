@@ -7,7 +7,7 @@ The pages name XAttention as one of the sparse operators Flux Attention's
 router can send a layer to: "XAttention: Block Sparse Attention with
 Antidiagonal Scoring" in the mlsanity page's reference list; a block-level
 operator with a block selection score used for prefill in the thelatestinai
-paper page's Table 4; the XA columns of its Table 12; and ``find_blocks_chunked``
+paper page's Table 3; the XA columns of its Table 12; and ``find_blocks_chunked``
 in an ``Xattention.py`` file of the codewithpapers function list.  They print
 none of its steps.  This module writes out the published method as read here
 (every point is a reading of the pages, labelled x1..x7):

@@ -4,7 +4,7 @@
 //
 // The pages name XAttention ("Block Sparse Attention with Antidiagonal
 // Scoring", mlsanity reference list) as a block-level sparse operator with a
-// block selection score for prefill [thelatestinai paper page, Table 4 and
+// block selection score for prefill [thelatestinai paper page, Table 3 and
 // Table 12]; its steps are the published method's, read as:
 //   reshaped rows: query row a stands for positions a*S + (S-1-s), key row b for
 //   positions b*S + s (s = 0..S-1, positions past the sequence are zero);
