@@ -437,6 +437,32 @@ def test_decode_llama_131k_sampled_heads():
 
 
 @pytest.mark.parametrize("bf16", [True, False])
+def test_decode_long_cache_many_splits(bf16):
+    """Caches of 600000 and 300001 tokens: the splits cap at 4096 tokens, so a
+    sequence has 147 of them (more than 64, the merge walks several chunks of
+    partials); FA and SA layers against the oracle on the whole row."""
+    B, hq, hkv, d, n = 2, 8, 2, 128, 600000
+    lengths = [n, 300001]
+    dt = "bf16" if bf16 else "f32"
+    kc = synth.device_normal((B, hkv, n, d), 41, dt)
+    vc = synth.device_normal((B, hkv, n, d), 42, dt)
+    q = synth.device_normal((B, hq, d), 43, dt)
+    cl = i32(lengths)
+    scale = 1 / math.sqrt(d)
+    bits = np.array([[1, 0], [1, 0]], np.uint8)
+    kh, vh, qh = host_of(kc), host_of(vc), host_of(q)
+    for layer in (0, 1):
+        o = torch.empty_like(q)
+        lse = torch.empty((B, hq), dtype=torch.float32, device=DEV)
+        _lib.fa_attn_decode(q, o, kc, vc, cl, u8(bits), layer, 128, 2048, 64, scale, lse=lse,
+                            route_host=bits)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.attn_decode(qh, kh, vh, lengths, bits, layer, 128, 2048, 64, scale)
+        assert max_err(host_of(o), o_ref) <= (TOL_BF16 if bf16 else TOL_F32), layer
+        assert np.abs(lse.cpu().numpy() - l_ref).max() <= (TOL_LSE if bf16 else TOL_F32), layer
+
+
+@pytest.mark.parametrize("bf16", [True, False])
 def test_route_host_kernels_match_device_route(bf16):
     """A host copy of the mask selects kernels compiled for all-FA / all-SA layers;
     their outputs must equal the device-route kernel bit for bit."""
