@@ -44,15 +44,15 @@ def test_router_on_the_benchmark_input():
     assert np.abs(logits.cpu().numpy() - l64).max() < 1e-5
 
 
-def sample_rows(n_random, seed, fa):
+def sample_rows(n_random, seed, fa, n=T):
     rng = np.random.default_rng(seed)
     if fa:  # the FA oracle costs O(T) per row: a few rows at each end and at random
-        rows = {0, 1, 63, 64, 2047, 2048, T - 65, T - 64, T - 2, T - 1}
+        rows = {0, 1, 63, 64, 2047, 2048, n - 65, n - 64, n - 2, n - 1}
     else:
-        rows = set(range(64)) | set(range(T - 64, T))
+        rows = set(range(64)) | set(range(n - 64, n))
         for edge in (SINK, WINDOW, SINK + WINDOW):
             rows |= {edge - 1, edge, edge + 1}
-    rows |= set(rng.integers(0, T, n_random).tolist())
+    rows |= set(rng.integers(0, n, n_random).tolist())
     return np.array(sorted(rows), np.int32)
 
 
@@ -75,6 +75,31 @@ def test_prefill_131k_sampled_rows(bit):
     torch.cuda.synchronize()
     rows = sample_rows(4 if bit else 200, seed=7 + bit, fa=bool(bit))
     o_ref, l_ref = oracle.attn_prefill(host_bf16(q), host_bf16(k), host_bf16(v), [0, T], r, 0,
+                                       SINK, WINDOW, BLOCK, scale, rows=rows)
+    got = synth.bf16_bits_to_f32(host_bf16(o)[rows]).astype(np.float64)
+    assert np.abs(got - o_ref).max() <= 2e-2
+    assert np.abs(lse.cpu().numpy()[rows] - l_ref).max() <= 1e-3
+
+
+@pytest.mark.parametrize("bit", [1, 0])
+def test_prefill_262k_sampled_rows(bit):
+    """The longest context the pages evaluate (RULER at 256K): one Llama-shaped
+    layer at 262144 tokens, FA and SA, through the per-kind kernels; every head
+    of sampled rows, the last ones included."""
+    hq, hkv, d, n = 32, 8, 128, 262144
+    q = synth.device_normal((n, hq, d), seed=110)
+    k = synth.device_normal((n, hkv, d), seed=111)
+    v = synth.device_normal((n, hkv, d), seed=112)
+    o = torch.empty_like(q)
+    lse = torch.empty((n, hq), dtype=torch.float32, device=DEV)
+    r = np.array([[bit]], np.uint8)
+    scale = 1 / math.sqrt(d)
+    _lib.fa_attn_prefill(q, k, v, o, torch.tensor([0, n], dtype=torch.int32, device=DEV), n,
+                         torch.tensor(r, device=DEV), 0, SINK, WINDOW, BLOCK, scale, lse=lse,
+                         route_host=r)
+    torch.cuda.synchronize()
+    rows = sample_rows(2 if bit else 100, seed=17 + bit, fa=bool(bit), n=n)
+    o_ref, l_ref = oracle.attn_prefill(host_bf16(q), host_bf16(k), host_bf16(v), [0, n], r, 0,
                                        SINK, WINDOW, BLOCK, scale, rows=rows)
     got = synth.bf16_bits_to_f32(host_bf16(o)[rows]).astype(np.float64)
     assert np.abs(got - o_ref).max() <= 2e-2
