@@ -45,7 +45,8 @@ def parse():
     p.add_argument("--decode-len", type=int, default=131072, help="KV cache length in decode")
     p.add_argument("--decode-batch", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-sweep", action="store_true", help="skip the 8k/32k/64k prefill sweep")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the 8k/32k/64k/256k prefill sweep")
     p.add_argument("--no-serving", action="store_true",
                    help="skip the batched decode sweep (batch 8/16/24/32 at a 32K context)")
     p.add_argument("--no-chunked", action="store_true",
@@ -450,6 +451,37 @@ def main():
         sweep.append({"seq": T, "tok_s": round(T / t_prefill, 1), "ms": round(t_prefill * 1e3, 3),
                       "n_fa_layers": n_fa, "all_fa_ms": round(t_prefill_allfa * 1e3, 3),
                       "speedup_vs_all_fa": round(t_prefill_allfa / t_prefill, 3)})
+        # twice the context (262144 at the defaults, the longest the pages evaluate),
+        # on inputs of its own: one set of Q/K/V for all layers, one pass of each kind
+        T2 = 2 * T
+        if T2 <= 262144:
+            x2 = synth.device_normal((T2, HIDDEN), seed=12)
+            q2 = synth.device_normal((T2, HQ, D), seed=120)
+            k2 = synth.device_normal((T2, HKV, D), seed=121)
+            v2 = synth.device_normal((T2, HKV, D), seed=122)
+            o2 = torch.empty_like(q2)
+            cu2 = torch.tensor([0, T2], dtype=torch.int32, device=dev)
+            res = {}
+            for kind in ("routed", "all_fa"):
+                a, b_ = ev(), ev()
+                a.record(stream)
+                _lib.fa_router_decide(x2, cu2, POOL, w1, b1, w2, b2, route, logits, ws_router)
+                r_host = (route.cpu().numpy() if kind == "routed"
+                          else np.ones((1, N_LAYERS), np.uint8))
+                r_dev = route if kind == "routed" else allfa
+                for l in range(N_LAYERS):
+                    _lib.fa_attn_prefill(q2, k2, v2, o2, cu2, T2, r_dev, l, SINK, WINDOW, BLOCK,
+                                         scale, route_host=r_host)
+                b_.record(stream)
+                torch.cuda.synchronize()
+                res[kind] = a.elapsed_time(b_)
+                if kind == "routed":
+                    n_fa_2 = int(route.cpu().numpy().sum())
+            sweep.append({"seq": T2, "tok_s": round(T2 / res["routed"] * 1e3, 1),
+                          "ms": round(res["routed"], 3), "n_fa_layers": n_fa_2,
+                          "all_fa_ms": round(res["all_fa"], 3),
+                          "speedup_vs_all_fa": round(res["all_fa"] / res["routed"], 3)})
+            del x2, q2, k2, v2, o2
         log("context sweep done")
 
     # ---- chunked prefill: the same routed 32-layer prefill in 16384-token chunks,
