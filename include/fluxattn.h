@@ -254,7 +254,8 @@ fa_status fa_attn_prefill_triangle(const void *q, const void *k, const void *v,
  *   P = softmax over b of A[a][.],
  *   scores[b][h][i][j] = sum of P over the 16 reshaped rows of query block i
  *                        and the 16 reshaped columns of key block j (j <= i).
- * q [total][n_q_heads][head_dim], k [total][n_kv_heads][head_dim], bf16.
+ * q [total][n_q_heads][head_dim], k [total][n_kv_heads][head_dim], bf16 (matrix
+ * cores) or fp32 (a plain VALU kernel, fp32 dot products), per dtype.
  * scores [batch][n_q_heads][n_qblocks][n_qblocks] fp32 out; entries with
  *   j > i or past a sequence's blocks are not written.
  * n_qblocks >= ceil(max_seqlen / block_tokens), <= 4096 (layout of scores).
@@ -262,7 +263,7 @@ fa_status fa_attn_prefill_triangle(const void *q, const void *k, const void *v,
  *   n_q_heads, n_qblocks) bytes (each reshaped row's partial sums of every
  *   key block, rescaled by a second kernel); caller-owned, contents undefined
  *   on return.
- * Supported: bf16, head_dim 64 or 128, stride 4 or 8 with block = 16 * stride,
+ * Supported: bf16 or fp32, head_dim 64 or 128, stride 4 or 8 with block = 16 * stride,
  * G in {1, 2, 4, 8, 16}.  Fixed reduction orders: repeated calls are bitwise
  * identical.
  * Errors: NULL pointer, batch/max_seqlen <= 0, bad heads, sm_scale not finite

@@ -296,8 +296,8 @@ fa_status fa_xattn_scores(const void *q, const void *k, int32_t dtype,
     if (n_qblocks < need || n_qblocks > 4096)
         return fail(FA_ERR_INVALID_ARG, "%s: n_qblocks %d must be in [%lld, 4096]", fn, n_qblocks,
                     (long long)need);
-    if (dtype != FA_BF16)
-        return fail(FA_ERR_UNSUPPORTED, "%s: dtype %d is not FA_BF16", fn, dtype);
+    if (dtype != FA_BF16 && dtype != FA_F32)
+        return fail(FA_ERR_UNSUPPORTED, "%s: dtype %d is not FA_F32/FA_BF16", fn, dtype);
     if (head_dim != 64 && head_dim != 128)
         return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", fn, head_dim);
     const int G = n_q_heads / n_kv_heads;
@@ -309,6 +309,7 @@ fa_status fa_xattn_scores(const void *q, const void *k, int32_t dtype,
                     workspace ? ws_bytes : (size_t)0, ws_need);
     fa::XaScoreArgs a{};
     a.workspace = workspace;
+    a.bf16 = dtype == FA_BF16;
     a.q = q;
     a.k = k;
     a.cu_seqlens = cu_seqlens;

@@ -99,7 +99,8 @@ hipError_t launch_kv_compact(const CompactArgs &a, hipStream_t stream);
 
 // XAttention branch: antidiagonal block scores and threshold selection
 struct XaScoreArgs {
-    const void *q, *k;              // bf16 [total][hq][d], [total][hkv][d]
+    const void *q, *k;              // [total][hq][d], [total][hkv][d]
+    bool bf16;                      // bf16 (MFMA kernel) or fp32 (VALU kernel)
     const int32_t *cu_seqlens;
     int batch, hq, hkv, d;
     int stride;                     // S; block = 16 S

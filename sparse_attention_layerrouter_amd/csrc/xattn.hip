@@ -324,6 +324,76 @@ __global__ __launch_bounds__(kXaWaves * 64) void xa_score_kernel(
     vm_wait_barrier(ic<0>{});
 }
 
+// fp32 inputs: the same partials from a plain VALU kernel.  One workgroup per
+// (query block i, head, sequence); thread (r, c) = (tid / 16, tid % 16) forms
+// A[16 i + r][16 j + c] for every key block j <= i as one fp32 dot product over
+// the S*d reshaped k-values (k index s*d + e), its query row staged in LDS.  The
+// 16 threads of a row then take the same online update as the MFMA kernel
+// (sum and max over the row's 16 columns in a fixed DPP order) and store the
+// row's (sum, max) of block j; the finishing kernel is shared.
+template <int D, int S>
+__global__ __launch_bounds__(256) void xa_score_f32_kernel(
+    const float *__restrict__ q, const float *__restrict__ k, const int32_t *__restrict__ cu,
+    int hq, int hkv, int nqb, float scale_log2, float2 *__restrict__ part,
+    float2 *__restrict__ rowstat)
+{
+    constexpr int RK = S * D;  // reshaped k-values per row
+    __shared__ __attribute__((aligned(16))) float qs[kXaRows][RK];
+    const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int r = tid >> 4, c = tid & 15;
+    const int start = cu[b];
+    const int T = cu[b + 1] - start;
+    const int nb = T > 0 ? (T + kXaRows * S - 1) / (kXaRows * S) : 0;
+    if (i >= nb) return;  // uniform
+    const int Tr = (T + S - 1) / S;
+    const int kvh = h / (hq / hkv);
+    // query rows of block i: reshaped row a = 16 i + rr, k index s*D + e holds
+    // position a*S + S-1-s (zero past the sequence)
+    for (int idx = tid; idx < kXaRows * RK / 4; idx += 256) {
+        const int rr = idx / (RK / 4), kk = (idx % (RK / 4)) * 4;
+        const int s = kk / D, e = kk % D;
+        const int pos = (i * kXaRows + rr) * S + (S - 1 - s);
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (pos < T) v = *(const float4 *)(q + ((size_t)(start + pos) * hq + h) * D + e);
+        *(float4 *)&qs[rr][kk] = v;
+    }
+    __syncthreads();
+    const int a = i * kXaRows + r;
+    const size_t ncell = (size_t)nqb * (nqb + 1) / 2;
+    float2 *pbase = part + (((size_t)b * hq + h) * ncell + (size_t)i * (i + 1) / 2) * kXaRows;
+    float m_row = -INFINITY, l_row = 0.0f;
+    for (int j = 0; j <= i; ++j) {  // uniform
+        const int bc = j * kXaRows + c;  // this thread's reshaped key column
+        float acc = 0.0f;
+        for (int s = 0; s < S; ++s) {
+            const int pos = bc * S + s;
+            if (pos >= T) break;  // zero rows past the sequence
+            const float *kr = k + ((size_t)(start + pos) * hkv + kvh) * D;
+#pragma unroll 4
+            for (int e = 0; e < D; e += 4) {
+                const float4 kv = *(const float4 *)(kr + e);
+                const float4 qv = *(const float4 *)&qs[r][s * D + e];
+                acc = __builtin_fmaf(qv.x, kv.x, acc);
+                acc = __builtin_fmaf(qv.y, kv.y, acc);
+                acc = __builtin_fmaf(qv.z, kv.z, acc);
+                acc = __builtin_fmaf(qv.w, kv.w, acc);
+            }
+        }
+        const bool ok = bc <= a && a < Tr;
+        const float v = acc * scale_log2;
+        const float mb = group_max<16>(ok ? v : -INFINITY);
+        const float m_new = fmaxf(m_row, mb);
+        const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
+        const float e = group_sum<16>(ok ? fast_exp2(v - m_sub) : 0.0f);
+        l_row = l_row * fast_exp2(m_row - m_sub) + e;
+        m_row = m_new;
+        if (c == 0) pbase[(size_t)j * kXaRows + r] = make_float2(e, m_new);
+    }
+    if (c == 0)
+        rowstat[(((size_t)b * hq + h) * nqb + i) * kXaRows + r] = make_float2(m_row, l_row);
+}
+
 // Block scores from the row partials: score[i][j] = sum over the 16 rows r of
 // block i of e_rj 2^(m_rj - M_r) / l_r, rows with l_r = 0 (past the sequence
 // end) left out.  One workgroup per (query block i, head, sequence); 8 lanes
@@ -506,6 +576,22 @@ hipError_t launch_scores_t(const XaScoreArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
+template <int D, int S>
+hipError_t launch_scores_f32_t(const XaScoreArgs &a, hipStream_t stream)
+{
+    float2 *part = (float2 *)a.workspace;
+    float2 *rowstat = part + xa_part_entries(a.batch, a.hq, a.nqb);
+    dim3 grid(a.nqb, a.hq, a.batch);
+    xa_score_f32_kernel<D, S><<<grid, 256, 0, stream>>>(
+        (const float *)a.q, (const float *)a.k, a.cu_seqlens, a.hq, a.hkv, a.nqb,
+        a.sm_scale / S * kLog2e, part, rowstat);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    xa_score_finish_kernel<<<grid, 256, 0, stream>>>(part, rowstat, a.cu_seqlens, a.hq, a.nqb,
+                                                     kXaRows * S, a.scores);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t xa_scores_workspace_bytes(int batch, int hq, int nqb)
@@ -515,6 +601,12 @@ size_t xa_scores_workspace_bytes(int batch, int hq, int nqb)
 
 hipError_t launch_xa_scores(const XaScoreArgs &a, hipStream_t stream)
 {
+    if (!a.bf16) {
+        if (a.d == 128) return a.stride == 8 ? launch_scores_f32_t<128, 8>(a, stream)
+                                             : launch_scores_f32_t<128, 4>(a, stream);
+        return a.stride == 8 ? launch_scores_f32_t<64, 8>(a, stream)
+                             : launch_scores_f32_t<64, 4>(a, stream);
+    }
     if (a.d == 128) return a.stride == 8 ? launch_scores_t<128, 8>(a, stream)
                                          : launch_scores_t<128, 4>(a, stream);
     return a.stride == 8 ? launch_scores_t<64, 8>(a, stream) : launch_scores_t<64, 4>(a, stream);

@@ -255,7 +255,7 @@ def test_xattn_workspace_size():
     (dict(nqb=7), _lib.FA_ERR_INVALID_ARG),          # fewer than ceil(1000 / 128)
     (dict(nqb=4097), _lib.FA_ERR_INVALID_ARG),
     (dict(stride=2, block=32), _lib.FA_ERR_UNSUPPORTED),
-    (dict(dtype=0), _lib.FA_ERR_UNSUPPORTED),
+    (dict(dtype=2), _lib.FA_ERR_UNSUPPORTED),
     (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
     (dict(hq=24, hkv=8), _lib.FA_ERR_UNSUPPORTED),   # G = 3
     (dict(ws=None), _lib.FA_ERR_WORKSPACE),

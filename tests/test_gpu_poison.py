@@ -111,13 +111,14 @@ def test_decode_reads_nothing_past_the_cache_length(bit, bf16):
     assert np.abs(l_got - l_ref).max() <= tol_lse
 
 
+@pytest.mark.parametrize("bf16", [True, False])
 @pytest.mark.parametrize("stride", [8, 4])
-def test_xattn_scores_read_nothing_past_the_last_sequence(stride):
+def test_xattn_scores_read_nothing_past_the_last_sequence(stride, bf16):
     rng = np.random.default_rng(41)
     lengths, hq, hkv, d = [700, 130, 1], 8, 2, 128
     block = 16 * stride
     cu = synth.cu_seqlens_of(lengths)
-    q, k, _ = synth.qkv_host(rng, int(cu[-1]), hq, hkv, d, bf16=True)
+    q, k, _ = synth.qkv_host(rng, int(cu[-1]), hq, hkv, d, bf16=bf16)
     scale = 1 / math.sqrt(d)
     nqb = -(-max(lengths) // block)
     sc = torch.zeros((len(lengths), hq, nqb, nqb), dtype=torch.float32, device=DEV)

@@ -83,6 +83,37 @@ def test_scores_and_selection_match_oracle(case):
         assert np.array_equal(keep, want), tau
 
 
+@pytest.mark.parametrize("case", [
+    ([1000, 333, 64, 1], 8, 2, 128, 8),
+    ([700, 129], 8, 2, 128, 4),
+    ([390, 200], 16, 2, 64, 8),
+    ([300], 4, 4, 64, 4),           # G = 1
+])
+def test_fp32_scores_and_selection_match_oracle(case):
+    """fp32 inputs take the VALU score kernel: scores within 1e-4 of the oracle,
+    selection bit-exact on them, the same partial sums and finishing kernel as bf16."""
+    lengths, hq, hkv, d, stride = case
+    block = 16 * stride
+    rng = np.random.default_rng(sum(lengths) + 3 * d + stride)
+    cu = synth.cu_seqlens_of(lengths)
+    q, k, _ = synth.qkv_host(rng, int(cu[-1]), hq, hkv, d, bf16=False)
+    scale = 1 / math.sqrt(d)
+    nqb = -(-max(lengths) // block)
+    got = run_scores(q, k, cu, block, stride, scale, nqb).cpu().numpy()
+    ref = xattn.block_scores(q, k, cu, block, stride, scale)
+    for b, T in enumerate(lengths):
+        nb = -(-T // block)
+        tri = np.tril(np.ones((nb, nb), bool))
+        assert np.abs(got[b][:, :nb, :nb][:, tri] - ref[b][:, :nb, :nb][:, tri]).max() <= 1e-4
+    nw = -(-nqb // 32)
+    m = torch.full((len(lengths), hq, nqb, nw), -1, dtype=torch.int32, device=DEV)
+    sc = torch.from_numpy(np.where(got < 0, 0, got).astype(np.float32)).to(DEV)
+    _lib.fa_xattn_select(sc, torch.tensor(cu, device=DEV), block, 0.9, m)
+    torch.cuda.synchronize()
+    want = xattn.select_blocks(np.where(got < 0, 0, got).astype(np.float32), lengths, block, 0.9)
+    assert np.array_equal(unpack(m.cpu().numpy(), nqb), want)
+
+
 def test_scores_are_deterministic():
     rng = np.random.default_rng(8)
     cu = synth.cu_seqlens_of([2048])
