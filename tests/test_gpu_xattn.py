@@ -114,6 +114,45 @@ def test_fp32_scores_and_selection_match_oracle(case):
     assert np.array_equal(unpack(m.cpu().numpy(), nqb), want)
 
 
+def test_padded_block_layout():
+    """n_qblocks above what the longest sequence needs (35 for 8 blocks, so the
+    mask rows take two words): the padding cells are never written, the selection
+    leaves their mask rows zero, and the masked prefill over the padded mask
+    equals the one over the tight layout bit for bit."""
+    rng = np.random.default_rng(35)
+    lengths, hq, hkv, d, block = [1000, 300], 8, 2, 128, 128
+    cu = synth.cu_seqlens_of(lengths)
+    q, k, v = synth.qkv_host(rng, int(cu[-1]), hq, hkv, d, bf16=True)
+    scale = 1 / math.sqrt(d)
+    tight = -(-max(lengths) // block)
+    nqb = 35
+    sc_t = run_scores(q, k, cu, block, 8, scale, tight).cpu().numpy()
+    sc_p = run_scores(q, k, cu, block, 8, scale, nqb)
+    got = sc_p.cpu().numpy()
+    for b, T in enumerate(lengths):
+        nb = -(-T // block)
+        tri = np.tril(np.ones((nb, nb), bool))
+        assert np.array_equal(got[b][:, :nb, :nb][:, tri], sc_t[b][:, :nb, :nb][:, tri])
+        assert (got[b][:, nb:] == -1.0).all()   # rows past the sequence: untouched
+        assert (got[b][:, :nb, nb:] == -1.0).all()
+    masks = {}
+    for n in (tight, nqb):
+        nw = -(-n // 32)
+        m = torch.full((len(lengths), hq, n, nw), -1, dtype=torch.int32, device=DEV)
+        src = sc_p if n == nqb else torch.from_numpy(sc_t).to(DEV)
+        _lib.fa_xattn_select(src, torch.tensor(cu, device=DEV), block, 0.9, m)
+        torch.cuda.synchronize()
+        masks[n] = m.cpu().numpy()
+    keep_t, keep_p = unpack(masks[tight], tight), unpack(masks[nqb], nqb)
+    for b, T in enumerate(lengths):
+        nb = -(-T // block)
+        assert np.array_equal(keep_p[b][:, :nb, :nb], keep_t[b][:, :nb, :nb])
+        assert not keep_p[b][:, nb:].any() and not keep_p[b][:, :, nb:].any()
+    o_t, l_t = run_xattn_prefill(q, k, v, cu, block, masks[tight], scale)
+    o_p, l_p = run_xattn_prefill(q, k, v, cu, block, masks[nqb], scale)
+    assert np.array_equal(o_t, o_p) and np.array_equal(l_t, l_p)
+
+
 def test_scores_are_deterministic():
     rng = np.random.default_rng(8)
     cu = synth.cu_seqlens_of([2048])
