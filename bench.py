@@ -53,6 +53,8 @@ def parse():
                    help="skip the chunked prefill (16384-token chunks over a growing key prefix)")
     p.add_argument("--no-xattn", action="store_true",
                    help="skip the XAttention sparse-branch timing (scores, selection, masked prefill)")
+    p.add_argument("--no-qwen", action="store_true",
+                   help="skip the Qwen3-4B-shaped varlen mixed-route leg")
     p.add_argument("--no-triangle", action="store_true",
                    help="skip the Triangle Attention sparse-branch timing")
     p.add_argument("--cpu-rows", type=int, default=192,
@@ -588,6 +590,87 @@ def main():
                                  "speedup_vs_fa_layer": round(t_fa * 1e3 / ms, 2)})
         log("triangle branch done")
 
+    # ---- Qwen3-4B-shaped mixed workload: 36 layers, a varlen batch of 4 sequences
+    # (16384 / 32768 / 49152 / 65536 tokens), a 2560 -> 256 -> 36 router giving
+    # per-sequence masks (FA and SA sequences share a launch where their bits
+    # differ), SA sink 128 / window 4096 / block 128; the routed prefill and its
+    # all-FA reference, then decode steps with the first token after the prompt
+    qwen = None
+    if not args.no_qwen and not args.profile and n_dec_layers == N_LAYERS:
+        QL, QHID, QSINK, QWIN, QBLK = 36, 2560, 128, 4096, 128
+        qlens = [16384, 32768, 49152, 65536]
+        qcu_np = synth.cu_seqlens_of(qlens)
+        qtot, qmax = int(qcu_np[-1]), max(qlens)
+        qcu = torch.from_numpy(qcu_np).to(dev)
+        xq = synth.device_normal((qtot, QHID), seed=51)
+        qw = [torch.from_numpy(a).to(dev)
+              for a in synth.router_weights(np.random.default_rng(52), QHID, ROUTER_HIDDEN, QL)]
+        qroute = torch.empty((4, QL), dtype=torch.uint8, device=dev)
+        qlogits = torch.empty((4, QL), dtype=torch.float32, device=dev)
+        ws_q = torch.empty(_lib.fa_router_workspace_size(4, QHID, ROUTER_HIDDEN),
+                           dtype=torch.uint8, device=dev)
+        qsets = [(synth.device_normal((qtot, HQ, D), seed=60 + 3 * i),
+                  synth.device_normal((qtot, HKV, D), seed=61 + 3 * i),
+                  synth.device_normal((qtot, HKV, D), seed=62 + 3 * i)) for i in range(2)]
+        qo = torch.empty_like(qsets[0][0])
+
+        def qwen_prefill(all_fa):
+            a, b_ = ev(), ev()
+            a.record(stream)
+            _lib.fa_router_decide(xq, qcu, POOL, *qw, qroute, qlogits, ws_q)
+            r_np = np.ones((4, QL), np.uint8) if all_fa else qroute.cpu().numpy()
+            r_dev = torch.from_numpy(r_np).to(dev) if all_fa else qroute
+            for l in range(QL):
+                q_, k_, v_ = qsets[l % 2]
+                _lib.fa_attn_prefill(q_, k_, v_, qo, qcu, qmax, r_dev, l, QSINK, QWIN, QBLK,
+                                     scale, route_host=r_np)
+            b_.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b_), r_np
+
+        qwen_prefill(False)  # warm-up
+        ms_q, qr_np = qwen_prefill(False)
+        ms_q_fa, _ = qwen_prefill(True)
+        # decode: caches are prefix views of the per-layer decode buffers above
+        QC = qmax + 8
+        n_el = 4 * HKV * QC * D
+        qcl = torch.tensor([n + 1 for n in qlens], dtype=torch.int32, device=dev)
+        qd = synth.device_normal((4, HQ, D), seed=63)
+        qod = torch.empty_like(qd)
+        ws_qd = torch.empty(_lib.fa_decode_workspace_size(4, HQ, D, QC), dtype=torch.uint8,
+                            device=dev)
+        dec_ms = {}
+        for kind in ("routed", "all_fa"):
+            r_np = qr_np if kind == "routed" else np.ones((4, QL), np.uint8)
+            r_dev = torch.from_numpy(r_np).to(dev)
+            times = []
+            for rep in range(4):  # one warm-up step, the median of three
+                a, b_ = ev(), ev()
+                a.record(stream)
+                for l in range(QL):
+                    kc, vc = caches[l % len(caches)]
+                    _lib.fa_attn_decode(qd, qod, kc.view(-1)[:n_el].view(4, HKV, QC, D),
+                                        vc.view(-1)[:n_el].view(4, HKV, QC, D), qcl, r_dev, l,
+                                        QSINK, QWIN, QBLK, scale, workspace=ws_qd,
+                                        route_host=r_np)
+                b_.record(stream)
+                torch.cuda.synchronize()
+                if rep:
+                    times.append(a.elapsed_time(b_))
+            dec_ms[kind] = float(np.median(times))
+        qwen = {"layers": QL, "lengths": qlens, "sink": QSINK, "window": QWIN, "block": QBLK,
+                "fa_layers_per_seq": [int(x) for x in qr_np.sum(axis=1)],
+                "mixed_layers": int(((qr_np.sum(axis=0) > 0) & (qr_np.sum(axis=0) < 4)).sum()),
+                "prefill_tok_s": round(qtot / ms_q * 1e3, 1), "prefill_ms": round(ms_q, 3),
+                "all_fa_prefill_ms": round(ms_q_fa, 3),
+                "prefill_speedup_vs_all_fa": round(ms_q_fa / ms_q, 3),
+                "decode_tok_s": round(4 / dec_ms["routed"] * 1e3, 1),
+                "decode_ms_per_step": round(dec_ms["routed"], 3),
+                "all_fa_decode_ms": round(dec_ms["all_fa"], 3),
+                "decode_speedup_vs_all_fa": round(dec_ms["all_fa"] / dec_ms["routed"], 3)}
+        del xq, qsets, qo
+        log("qwen3-4b varlen leg done")
+
     # ---- roofline --------------------------------------------------------------
     fa_flop = flops_of_pairs(pairs_fa(T))
     sa_flop = flops_of_pairs(pairs_sa(T))
@@ -635,6 +718,7 @@ def main():
             "chunked_16k": chunked,
             "xattn_branch": xattn,
             "triangle_branch": tri,
+            "qwen3_4b_varlen": qwen,
         },
         "decode": {
             "tok_s": round(NB / t_decode, 1),

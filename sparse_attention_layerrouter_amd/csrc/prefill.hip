@@ -179,16 +179,30 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     const int half = lane >> 5;
     const int l32 = lane & 31;
 
-    // blockIdx -> (position tile, head group, unit) with the unit (sequence, kv
-    // head) fastest, so consecutive workgroups -- which the dispatcher spreads
-    // round-robin over the 8 XCDs -- keep one KV head per XCD when the unit
-    // count is a multiple of 8.  Position tiles run last-first: the causal tail
-    // tiles carry the most KV tiles and start first.
-    int bid = blockIdx.x;
-    const int unit = bid % n_units;
-    bid /= n_units;
-    const int hg = bid % n_hgroups;
-    const int ptile = n_ptiles - 1 - bid / n_hgroups;
+    // blockIdx -> (unit (sequence, kv head), head group, position tile).  The
+    // dispatcher deals consecutive workgroups round-robin to the 8 XCDs, each
+    // with its own L2.  When the unit count is a multiple of 8, XCD x (blockIdx
+    // mod 8) walks the units 8u + x one at a time, all of a unit's workgroups
+    // before the next, so its CUs stream one KV head's tiles in step and share
+    // them in L2 (a varlen batch would otherwise interleave its sequences on
+    // every XCD).  Otherwise the unit is the fastest index.  Within a unit,
+    // position tiles run last-first: the causal tail tiles carry the most KV
+    // tiles and start first.
+    int unit, hg, ptile;
+    if (n_units % 8 == 0) {  // uniform
+        const int m = blockIdx.x >> 3;
+        const int per_unit = n_hgroups * n_ptiles;
+        const int u = m / per_unit, rem = m - u * per_unit;
+        unit = 8 * u + (blockIdx.x & 7);
+        hg = rem % n_hgroups;
+        ptile = n_ptiles - 1 - rem / n_hgroups;
+    } else {
+        int bid = blockIdx.x;
+        unit = bid % n_units;
+        bid /= n_units;
+        hg = bid % n_hgroups;
+        ptile = n_ptiles - 1 - bid / n_hgroups;
+    }
     const int b = unit / hkv, kvh = unit % hkv;
 
     // Query rows of sequence b are cu[b] .. cu[b+1]-1 and its keys cu_k[b] ..
