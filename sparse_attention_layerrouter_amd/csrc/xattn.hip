@@ -137,11 +137,25 @@ __global__ __launch_bounds__(kXaWaves * 64) void xa_score_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave >> 2, wq = wave & 3;
-    int bid = blockIdx.x;
-    const int unit = bid % n_units;
-    bid /= n_units;
-    const int hg = bid % n_hgroups;
-    const int pm = npairs - 1 - bid / n_hgroups;  // block pair; the heavy ones start first
+    // unit (sequence, kv head), head group, block pair: as in the prefill
+    // kernels, XCD x (blockIdx mod 8) walks the units 8u + x one at a time when
+    // the unit count is a multiple of 8, so its CUs share one key stream in L2;
+    // the heavy block pairs start first
+    int unit, hg, pm;
+    if (n_units % 8 == 0) {  // uniform
+        const int m = blockIdx.x >> 3;
+        const int per_unit = n_hgroups * npairs;
+        const int u = m / per_unit, rem = m - u * per_unit;
+        unit = 8 * u + (blockIdx.x & 7);
+        hg = rem % n_hgroups;
+        pm = npairs - 1 - rem / n_hgroups;
+    } else {
+        int bid = blockIdx.x;
+        unit = bid % n_units;
+        bid /= n_units;
+        hg = bid % n_hgroups;
+        pm = npairs - 1 - bid / n_hgroups;
+    }
     const int b = unit / hkv, kvh = unit % hkv;
     const int start = cu[b];
     const int T = cu[b + 1] - start;
