@@ -163,3 +163,76 @@ def device_positional_qkv(T: int, hq: int, hkv: int, d: int, seed: int, alpha: f
     k = draw(hkv, True)
     v = draw(hkv, False)
     return q, k, v
+
+
+def _needle_positions(t, n_heads: int, gen, n_first: int, n_recent: int):
+    """One key position per (query position, head) for the needle inputs below.
+
+    t: int64 tensor of query positions.  Even heads draw uniformly from [0, t]
+    (anywhere in the causal past); odd heads draw, with even odds, from the first
+    min(t + 1, n_first) positions or from the last n_recent positions up to t.
+    Returns an int64 tensor [len(t), n_heads]."""
+    import torch
+
+    dev = t.device
+    n = t.numel()
+    u_far = torch.rand((n, n_heads), generator=gen, device=dev, dtype=torch.float64)
+    u_near = torch.rand((n, n_heads), generator=gen, device=dev, dtype=torch.float64)
+    pick_first = torch.rand((n, n_heads), generator=gen, device=dev) < 0.5
+    tt = t[:, None]
+    far = torch.minimum(torch.floor(u_far * (tt + 1).double()).long(), tt)
+    n_f = torch.clamp(tt + 1, max=n_first)
+    first = torch.minimum(torch.floor(u_near * n_f.double()).long(), n_f - 1)
+    lo = torch.clamp(tt - (n_recent - 1), min=0)
+    recent = torch.minimum(lo + torch.floor(u_near * (tt - lo + 1).double()).long(), tt)
+    near = torch.where(pick_first, first, recent)
+    even = (torch.arange(n_heads, device=dev) % 2 == 0)[None, :]
+    return torch.where(even, far, near)
+
+
+def device_needle_qkv(T: int, hq: int, hkv: int, d: int, seed: int, beta: float = 2.0,
+                      n_first: int = 128, n_recent: int = 64, device: str = "cuda:0"):
+    """bf16 Q, K, V [T, heads, d] in which every query row points at one earlier key.
+
+    K and V are N(0,1).  Query row t of head h is beta * K[g][h // G] (G = hq / hkv),
+    a copy of the key at a drawn position g <= t (see _needle_positions); beta = 2
+    scales bf16 values exactly.  That key's score (about beta * d / sqrt(d)) stands
+    far above the others, so a row's output is close to one V row, a vector of
+    size O(1): a dropped, misplaced or mis-read key/value tile moves the output by
+    O(1) instead of by O(1/sqrt(T)) as with i.i.d. inputs.  Returns (q, k, v, g)
+    with g the int64 positions [T, hq]."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    k = torch.randn((T, hkv, d), generator=gen, device=device, dtype=torch.float32)
+    k = k.to(torch.bfloat16)
+    v = torch.randn((T, hkv, d), generator=gen, device=device, dtype=torch.float32)
+    v = v.to(torch.bfloat16)
+    t = torch.arange(T, device=device, dtype=torch.int64)
+    g = _needle_positions(t, hq, gen, n_first, n_recent)
+    kvh = (torch.arange(hq, device=device) // (hq // hkv))[None, :]
+    q = k[g, kvh] * beta
+    return q.contiguous(), k, v, g
+
+
+def device_needle_decode_q(k_cache, hq: int, cache_len, seed: int, beta: float = 2.0,
+                           n_first: int = 128, n_recent: int = 64):
+    """Decode queries [B, hq, d] (bf16) pointing at one cached key each.
+
+    k_cache [B, hkv, max_cache, d] bf16; cache_len: host sequence of the cache
+    lengths n_b (the query sits at position n_b - 1).  Query head h of sequence b
+    is beta * k_cache[b][h // G][g], g drawn as in _needle_positions with
+    t = n_b - 1.  Returns (q, g)."""
+    import torch
+
+    dev = k_cache.device
+    B, hkv = k_cache.shape[0], k_cache.shape[1]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    t = torch.tensor([int(n) - 1 for n in cache_len], device=dev, dtype=torch.int64)
+    g = _needle_positions(t, hq, gen, n_first, n_recent)
+    b_idx = torch.arange(B, device=dev)[:, None]
+    kvh = (torch.arange(hq, device=dev) // (hq // hkv))[None, :]
+    q = k_cache[b_idx, kvh, g] * beta
+    return q.contiguous(), g
