@@ -259,6 +259,9 @@ fa_status fa_attn_prefill_triangle(const void *q, const void *k, const void *v,
  * scores [batch][n_q_heads][n_qblocks][n_qblocks] fp32 out; entries with
  *   j > i or past a sequence's blocks are not written.
  * n_qblocks >= ceil(max_seqlen / block_tokens), <= 4096 (layout of scores).
+ *   Device behaviour: the query blocks of a sequence at or past n_qblocks (a
+ *   sequence longer than max_seqlen promised) are not computed; nothing is
+ *   written outside the (sequence, head) rows of the layout.
  * workspace: device scratch of at least fa_xattn_workspace_size(batch,
  *   n_q_heads, n_qblocks) bytes (each reshaped row's partial sums of every
  *   key block, rescaled by a second kernel); caller-owned, contents undefined
@@ -294,7 +297,8 @@ size_t fa_xattn_workspace_size(int32_t batch, int32_t n_q_heads,
  * ascending j, the kept sum in the order blocks join, so the decision is a
  * fixed function of the fp32 scores.
  * mask [batch][n_q_heads][n_qblocks][ceil(n_qblocks / 32)] uint32 out: bit j
- *   of row i set iff key block j is kept; rows past a sequence are zero.
+ *   of row i set iff key block j is kept; rows past a sequence are zero (a
+ *   sequence with more than n_qblocks blocks keeps only its first n_qblocks).
  * Errors: NULL pointer, batch/heads/block <= 0, n_qblocks outside [1, 4096],
  * threshold not finite or <= 0 -> FA_ERR_INVALID_ARG.
  */

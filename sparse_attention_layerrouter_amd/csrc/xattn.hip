@@ -36,17 +36,10 @@ namespace fa {
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
-constexpr int kXaRows = 16;  // reshaped rows (and columns) per block: B = 16 S
 constexpr int kXaRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kXaLook = 8;                // LDS operand reads in flight
 constexpr int kXaWaves = 8;
 
-// row partials of the single score pass: one (sum, max) pair per reshaped row of
-// every cell j <= i of every (sequence, head), cells of row i at i (i+1) / 2
-__host__ __device__ inline size_t xa_part_entries(int batch, int hq, int nqb)
-{
-    return (size_t)batch * hq * ((size_t)nqb * (nqb + 1) / 2) * kXaRows;
-}
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c)
 {
@@ -159,7 +152,8 @@ __global__ __launch_bounds__(kXaWaves * 64) void xa_score_kernel(
     const int b = unit / hkv, kvh = unit % hkv;
     const int start = cu[b];
     const int T = cu[b + 1] - start;
-    const int nb = (T + B - 1) / B;
+    // blocks at or past nqb (a sequence longer than the layout holds) are not computed
+    const int nb = min((T + B - 1) / B, nqb);
     if (2 * pm >= nb) return;                 // uniform
     const int i = 2 * pm + grp;               // this wave's query block
     const int j_last = min(2 * pm + 1, nb - 1);  // last key block of the workgroup
@@ -358,7 +352,7 @@ __global__ __launch_bounds__(256) void xa_score_f32_kernel(
     const int r = tid >> 4, c = tid & 15;
     const int start = cu[b];
     const int T = cu[b + 1] - start;
-    const int nb = T > 0 ? (T + kXaRows * S - 1) / (kXaRows * S) : 0;
+    const int nb = T > 0 ? min((T + kXaRows * S - 1) / (kXaRows * S), nqb) : 0;
     if (i >= nb) return;  // uniform
     const int Tr = (T + S - 1) / S;
     const int kvh = h / (hq / hkv);
@@ -420,7 +414,7 @@ __global__ __launch_bounds__(256) void xa_score_finish_kernel(
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const int T = cu[b + 1] - cu[b];
-    const int nb = T > 0 ? (T + block - 1) / block : 0;
+    const int nb = T > 0 ? min((T + block - 1) / block, nqb) : 0;
     if (i >= nb) return;
     __shared__ float2 st[kXaRows];  // (M_r, 1 / l_r), 1 / l_r = 0 marking an empty row
     if (tid < kXaRows) {
@@ -472,7 +466,7 @@ __global__ __launch_bounds__(256) void xa_select_kernel(const float *__restrict_
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const int T = cu[b + 1] - cu[b];
-    const int nb = T > 0 ? (T + block - 1) / block : 0;
+    const int nb = T > 0 ? min((T + block - 1) / block, nqb) : 0;
     uint32_t *mrow = mask + (((size_t)b * hq + h) * nqb + i) * nw;
     for (int w = tid; w < nw; w += 256) bits[w] = 0u;
     if (i >= nb) {
@@ -607,11 +601,6 @@ hipError_t launch_scores_f32_t(const XaScoreArgs &a, hipStream_t stream)
 }
 
 }  // namespace
-
-size_t xa_scores_workspace_bytes(int batch, int hq, int nqb)
-{
-    return (xa_part_entries(batch, hq, nqb) + (size_t)batch * hq * nqb * kXaRows) * sizeof(float2);
-}
 
 hipError_t launch_xa_scores(const XaScoreArgs &a, hipStream_t stream)
 {

@@ -402,3 +402,39 @@ def test_tile_past_the_sequence_end_reads_nothing(bf16):
     got = as_f64(oh)
     assert np.isfinite(got).all() and np.isfinite(lse.cpu().numpy()).all()
     assert np.abs(got - o_ref).max() <= (2e-2 if bf16 else 1e-4)
+
+
+def test_sequence_longer_than_the_block_layout():
+    """A sequence with more blocks than n_qblocks (1400 tokens = 11 blocks of 128 in a
+    9-block layout, longer than the max_seqlen the call promises), beside a short one,
+    with an odd n_qblocks: the first 9 query blocks of every head match the oracle,
+    the cells of the layout past each row stay unwritten, the workspace tail past its
+    stated size is untouched, and the selection keeps only blocks below n_qblocks."""
+    rng = np.random.default_rng(1400)
+    lengths, hq, hkv, d, stride, block, nqb = [1400, 300], 8, 2, 128, 8, 128, 9
+    cu = synth.cu_seqlens_of(lengths)
+    q, k, _ = synth.qkv_host(rng, int(cu[-1]), hq, hkv, d, bf16=True)
+    scale = 1 / math.sqrt(d)
+    sc = torch.full((2, hq, nqb, nqb), -1.0, dtype=torch.float32, device=DEV)
+    need = _lib.fa_xattn_workspace_size(2, hq, nqb)
+    ws = torch.full((need + 4096,), 0x5A, dtype=torch.uint8, device=DEV)
+    _lib.fa_xattn_scores(dev_from(q), dev_from(k), torch.tensor(cu, device=DEV),
+                         nqb * block - 100, block, stride, scale, sc, workspace=ws)
+    torch.cuda.synchronize()
+    assert (ws[need:].cpu().numpy() == 0x5A).all()
+    got = sc.cpu().numpy()
+    ref = xattn.block_scores(q, k, cu, block, stride, scale)
+    for b, T in enumerate(lengths):
+        nb = min(-(-T // block), nqb)
+        tri = np.tril(np.ones((nb, nb), bool))
+        assert np.abs(got[b][:, :nb, :nb][:, tri] - ref[b][:, :nb, :nb][:, tri]).max() <= 1e-4
+        assert (got[b][:, :nb, :nb][:, ~tri] == -1.0).all()
+        assert (got[b][:, nb:] == -1.0).all()
+    nw = -(-nqb // 32)
+    m = torch.full((2, hq, nqb, nw), -1, dtype=torch.int32, device=DEV)
+    _lib.fa_xattn_select(sc, torch.tensor(cu, device=DEV), block, 0.9, m)
+    torch.cuda.synchronize()
+    keep = unpack(m.cpu().numpy(), nqb)
+    want = xattn.select_blocks(np.where(got < 0, 0, got).astype(np.float32),
+                               [min(T, nqb * block) for T in lengths], block, 0.9)
+    assert np.array_equal(keep, want)
