@@ -382,13 +382,16 @@ def test_sm_scale_scales_scores():
 
 def test_decode_equals_last_prefill_row():
     """Decode over an n-token cache equals row n-1 of prefill on the same tokens,
-    for FA and SA, several cache lengths and a padded cache."""
+    for FA and SA, several cache lengths and a padded cache.  Lengths that are
+    multiples of the block (192, 64) put the query at the last position of a
+    block, where a query placed one position late would fall in the next block
+    and move the SA window."""
     rng = np.random.default_rng(11)
-    B, Hq, Hkv, d, max_cache = 3, 4, 2, 16, 200
-    lengths = [200, 97, 1]
+    B, Hq, Hkv, d, max_cache = 5, 4, 2, 16, 200
+    lengths = [200, 97, 1, 192, 64]
     kc, vc = synth.kv_cache_host(rng, B, Hkv, max_cache, d, bf16=False)
     qd = synth.normal(rng, (B, Hq, d))
-    route = np.array([[1, 0], [0, 1], [0, 0]], np.uint8)
+    route = np.array([[1, 0], [0, 1], [0, 0], [0, 0], [1, 0]], np.uint8)
     for layer in (0, 1):
         o, lse = oracle.attn_decode(qd, kc, vc, lengths, route, layer, 16, 48, 16, 0.25)
         for b, n in enumerate(lengths):
