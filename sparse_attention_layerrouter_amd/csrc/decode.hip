@@ -21,16 +21,6 @@
 
 namespace fa {
 
-int decode_split_tokens(int max_kept_tokens)
-{
-    // about 64 splits per (sequence, kv head); 128..4096 tokens per split
-    int st = (max_kept_tokens + 63) / 64;
-    st = (st + 63) / 64 * 64;
-    if (st < 128) st = 128;
-    if (st > 4096) st = 4096;
-    return st;
-}
-
 namespace {
 
 constexpr int kThreads = 256;

@@ -109,7 +109,20 @@ struct XaScoreArgs {
     float *scores;                  // [batch][hq][nqb][nqb]
     void *workspace;                // xa_scores_workspace_bytes(batch, hq, nqb)
 };
-size_t xa_scores_workspace_bytes(int batch, int hq, int nqb);
+// Score workspace: one (sum, max) float pair per reshaped row of every cell
+// j <= i of every (sequence, head), the cells of query block i starting at cell
+// i (i + 1) / 2; then one (max, sum) pair per reshaped row of every (sequence,
+// head, query block).  kXaRows reshaped rows (and columns) per block: B = 16 S.
+constexpr int kXaRows = 16;
+inline size_t xa_part_entries(int batch, int hq, int nqb)
+{
+    return (size_t)batch * hq * ((size_t)nqb * (nqb + 1) / 2) * kXaRows;
+}
+inline size_t xa_scores_workspace_bytes(int batch, int hq, int nqb)
+{
+    return (xa_part_entries(batch, hq, nqb) + (size_t)batch * hq * nqb * kXaRows) *
+           (2 * sizeof(float));
+}
 hipError_t launch_xa_scores(const XaScoreArgs &a, hipStream_t stream);
 
 struct XaSelectArgs {
@@ -121,8 +134,16 @@ struct XaSelectArgs {
 };
 hipError_t launch_xa_select(const XaSelectArgs &a, hipStream_t stream);
 
-// Split policy shared by fa_decode_workspace_size and fa_attn_decode.
-int decode_split_tokens(int max_kept_tokens);
+// Split policy shared by fa_decode_workspace_size and fa_attn_decode: about 64
+// splits per (sequence, kv head), 128..4096 tokens per split, a multiple of 64.
+inline int decode_split_tokens(int max_kept_tokens)
+{
+    int st = (max_kept_tokens + 63) / 64;
+    st = (st + 63) / 64 * 64;
+    if (st < 128) st = 128;
+    if (st > 4096) st = 4096;
+    return st;
+}
 inline int decode_n_splits(int max_kept_tokens)
 {
     int st = decode_split_tokens(max_kept_tokens);
