@@ -11,6 +11,14 @@ One step = the whole hot path on one batch of synthetic, HBM-resident input:
      (even layers FA, odd layers SA, same sparse configuration).
 The prefill throughput of step 1+2 is `value` (tok/s at 128k); decode tok/s is
 reported beside it.  Inputs are N(0, 1) drawn on the device from fixed seeds.
+Per-layer and per-step times are reported as median / p10 / p90 over the timed
+steps (the pages' protocol: warm-up iterations, then timed ones, medians).
+
+Other legs: a context sweep, chunked prefill, ring caches, a batched-serving
+sweep, the XAttention and Triangle Attention branches, single FA/SA layers at
+32K, and the Qwen3-4B-shaped varlen workload (prefill, then 256 decode steps
+that append to its caches); `--only-qwen` runs that workload alone and
+`--cpu-full` runs the unsampled oracle timings and full-row parity.
 
 Prints ONE JSON line.  `--gpus` above 1 is refused: this path runs on one GPU.
 """
@@ -57,6 +65,15 @@ def parse():
                    help="skip the Qwen3-4B-shaped varlen mixed-route leg")
     p.add_argument("--no-triangle", action="store_true",
                    help="skip the Triangle Attention sparse-branch timing")
+    p.add_argument("--no-config2", action="store_true",
+                   help="skip the single FA / SA layer timing at 32768 tokens")
+    p.add_argument("--only-qwen", action="store_true",
+                   help="run only the Qwen3-4B-shaped varlen leg (prefill + decode loop)")
+    p.add_argument("--qwen-steps", type=int, default=256,
+                   help="decode steps per sequence in the Qwen3-4B leg (each appends a token)")
+    p.add_argument("--cpu-full", action="store_true",
+                   help="only the unsampled oracle timings (tiny case, one SA layer at 32K, one "
+                        "FA and one SA decode layer at batch 8 x 131072), with full-row parity")
     p.add_argument("--cpu-rows", type=int, default=192,
                    help="query rows of the FA layer the oracle times (SA gets 4x)")
     p.add_argument("--profile", action="store_true",
@@ -136,6 +153,36 @@ def log(msg: str):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
+def dist(values_ms):
+    """median / p10 / p90 / mean of a list of times in ms."""
+    import numpy as np
+
+    a = np.asarray(values_ms, dtype=np.float64)
+    if a.size == 0:
+        return None
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "mean": round(float(a.mean()), 4),
+            "n": int(a.size)}
+
+
+def cpu_info():
+    """Host CPU model and the number of cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return model, cores
+
+
 # ---------------------------------------------------------------------------
 
 def main():
@@ -163,6 +210,12 @@ def main():
         print(json.dumps({"copy_probe_bytes_each_way": x.numel() * 4}))
         return
     stream = torch.cuda.current_stream()
+    if args.only_qwen:
+        print(json.dumps({"qwen3_4b_varlen": qwen_leg(args, stream)}))
+        return
+    if args.cpu_full:
+        print(json.dumps({"cpu_full": cpu_full(stream)}))
+        return
     T = args.seq
     NB, NC = args.decode_batch, args.decode_len
     if args.profile:
@@ -252,7 +305,17 @@ def main():
         for _ in range(2):
             step(prefill_route=torch.tensor([[1, 0] + [0] * 30], dtype=torch.uint8, device=dev))
         torch.cuda.synchronize()
-        print(json.dumps({"profile_run": True, "seq": T, "decode_cache": NC}))
+        kept_sa = kept_tokens_decode(NC, False)
+        alg = {
+            "prefill_bf16_fa_131k": {"flop": flops_of_pairs(pairs_fa(T))},
+            "prefill_bf16_sa_131k": {"flop": flops_of_pairs(pairs_sa(T))},
+            "decode_bf16_fa_131k": {"flop": 4.0 * NB * HQ * NC * D,
+                                    "bytes": NB * HKV * NC * D * 4 + 2 * NB * HQ * D * 2},
+            "decode_bf16_sa_131k": {"flop": 4.0 * NB * HQ * kept_sa * D,
+                                    "bytes": NB * HKV * kept_sa * D * 4 + 2 * NB * HQ * D * 2},
+        }
+        print(json.dumps({"profile_run": True, "seq": T, "decode_cache": NC,
+                          "decode_batch": NB, "algorithmic": alg}))
         return
 
     for _ in range(args.warmup):
@@ -272,9 +335,11 @@ def main():
     logits_np = logits.cpu().numpy()[0]
     n_fa = int(route_np.sum())
 
-    t_router = np.mean([a.elapsed_time(b) for (a, b), _, _ in recs]) * 1e-3
-    pre_t = np.array([[a.elapsed_time(b) * 1e-3 for a, b in pre] for _, pre, _ in recs])
-    dec_t = np.array([[a.elapsed_time(b) * 1e-3 for a, b in dec] for _, _, dec in recs])
+    router_ms = np.array([a.elapsed_time(b) for (a, b), _, _ in recs])
+    pre_ms = np.array([[a.elapsed_time(b) for a, b in pre] for _, pre, _ in recs])
+    dec_ms = np.array([[a.elapsed_time(b) for a, b in dec] for _, _, dec in recs])
+    t_router = float(router_ms.mean()) * 1e-3
+    pre_t, dec_t = pre_ms * 1e-3, dec_ms * 1e-3
     t_prefill = t_router + pre_t.sum(axis=1).mean()
     t_decode = dec_t.sum(axis=1).mean()
     fa_layers = [l for l in range(N_LAYERS) if route_np[l]]
@@ -285,24 +350,49 @@ def main():
     dec_sa = [l for l in range(N_LAYERS) if not dec_route_np[0, l]]
     td_fa = float(dec_t[:, dec_fa].mean())
     td_sa = float(dec_t[:, dec_sa].mean())
+    timing = {
+        "protocol": (f"{args.warmup} warm-up steps, then {args.steps} timed steps; HIP events "
+                     f"around every call on the launch stream; ms"),
+        "prefill_step_ms": dist(router_ms + pre_ms.sum(axis=1)),
+        "router_ms": dist(router_ms),
+        "prefill_fa_layer_ms": dist(pre_ms[:, fa_layers].ravel()) if fa_layers else None,
+        "prefill_sa_layer_ms": dist(pre_ms[:, sa_layers].ravel()) if sa_layers else None,
+        "decode_step_ms": dist(dec_ms.sum(axis=1)),
+        "decode_fa_layer_us": dist(dec_ms[:, dec_fa].ravel() * 1e3),
+        "decode_sa_layer_us": dist(dec_ms[:, dec_sa].ravel() * 1e3),
+    }
 
-    # measured all-FA references (one pass each, same events)
+    # measured all-FA references: prefill with every layer FA (the same per-kind FA
+    # kernel as the routed step's FA layers), one warm-up pass and up to three timed;
+    # decode with every layer FA through the FA kernel (host route copy), with the
+    # routed step's warm-up and timed counts
     allfa = torch.ones((1, N_LAYERS), dtype=torch.uint8, device=dev)
     ref = []
-    step(ref, prefill_route=allfa)
+    for rep in range(1 + min(3, args.steps)):
+        step(ref if rep else None, prefill_route=allfa)
     torch.cuda.synchronize()
-    (ra, rb), pre_ref, _ = ref[0]
-    t_prefill_allfa = ra.elapsed_time(rb) * 1e-3 + sum(a.elapsed_time(b) for a, b in pre_ref) * 1e-3
-    dec_allfa_route = torch.ones((NB, N_LAYERS), dtype=torch.uint8, device=dev)
-    a, b = ev(), ev()
-    a.record(stream)
-    for l in range(N_LAYERS):
-        kc, vc = caches[l]
-        _lib.fa_attn_decode(q_dec, o_dec, kc, vc, cache_len, dec_allfa_route, l, SINK, WINDOW,
-                            BLOCK, scale, workspace=ws_dec)
-    b.record(stream)
-    torch.cuda.synchronize()
-    t_decode_allfa = a.elapsed_time(b) * 1e-3
+    allfa_pre_ms = [ra.elapsed_time(rb) + sum(a.elapsed_time(b) for a, b in pre_ref)
+                    for (ra, rb), pre_ref, _ in ref]
+    t_prefill_allfa = float(np.median(allfa_pre_ms)) * 1e-3
+    dec_allfa_np = np.ones((NB, N_LAYERS), np.uint8)
+    dec_allfa_route = torch.from_numpy(dec_allfa_np).to(dev)
+    allfa_dec_ms = []
+    for rep in range(args.warmup + args.steps):
+        a, b = ev(), ev()
+        a.record(stream)
+        for l in range(n_dec_layers):
+            kc, vc = caches[l]
+            _lib.fa_attn_decode(q_dec, o_dec, kc, vc, cache_len, dec_allfa_route, l, SINK,
+                                WINDOW, BLOCK, scale, workspace=ws_dec,
+                                route_host=dec_allfa_np)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if rep >= args.warmup:
+            allfa_dec_ms.append(a.elapsed_time(b))
+    t_decode_allfa = float(np.median(allfa_dec_ms)) * 1e-3
+    t_decode_med = float(np.median(dec_ms.sum(axis=1))) * 1e-3
+    timing["all_fa_prefill_ms"] = dist(allfa_pre_ms)
+    timing["all_fa_decode_step_ms"] = dist(allfa_dec_ms)
 
     log("all-FA references done")
 
@@ -388,7 +478,8 @@ def main():
             graph_ok = bool(torch.equal(o_s.view(torch.int16), o_eager.view(torch.int16)))
             del g
             # the all-FA reference on the same caches
-            r_fa = torch.ones((bs, N_LAYERS), dtype=torch.uint8, device=dev)
+            r_fa_np = np.ones((bs, N_LAYERS), np.uint8)
+            r_fa = torch.from_numpy(r_fa_np).to(dev)
             times = []
             for rep in range(6):
                 a, b_ = ev(), ev()
@@ -398,7 +489,8 @@ def main():
                     n_el = bs * HKV * SC * D
                     _lib.fa_attn_decode(q_s, o_s, kc.view(-1)[:n_el].view(bs, HKV, SC, D),
                                         vc.view(-1)[:n_el].view(bs, HKV, SC, D), cl_s, r_fa, l,
-                                        SINK, WINDOW, BLOCK, scale, workspace=ws_s)
+                                        SINK, WINDOW, BLOCK, scale, workspace=ws_s,
+                                        route_host=r_fa_np)
                 b_.record(stream)
                 torch.cuda.synchronize()
                 if rep:
@@ -590,85 +682,22 @@ def main():
                                  "speedup_vs_fa_layer": round(t_fa * 1e3 / ms, 2)})
         log("triangle branch done")
 
-    # ---- Qwen3-4B-shaped mixed workload: 36 layers, a varlen batch of 4 sequences
-    # (16384 / 32768 / 49152 / 65536 tokens), a 2560 -> 256 -> 36 router giving
-    # per-sequence masks (FA and SA sequences share a launch where their bits
-    # differ), SA sink 128 / window 4096 / block 128; the routed prefill and its
-    # all-FA reference, then decode steps with the first token after the prompt
+    # ---- single FA and SA layers at 32768 tokens (one Llama-shaped layer run as
+    # each kind), 10 warm-up and 50 timed calls
+    config2 = None
+    if not args.no_config2 and T >= 32768:
+        config2 = config2_leg(stream, sets[0])
+        log("32K single-layer leg done")
+
+    # ---- Qwen3-4B-shaped mixed workload (prefill, then a decode loop appending to
+    # its own caches); the Llama decode caches are not needed past this point
+    caches.clear()
+    rings.clear()
+    torch.cuda.empty_cache()
     qwen = None
     if not args.no_qwen and not args.profile and n_dec_layers == N_LAYERS:
-        QL, QHID, QSINK, QWIN, QBLK = 36, 2560, 128, 4096, 128
-        qlens = [16384, 32768, 49152, 65536]
-        qcu_np = synth.cu_seqlens_of(qlens)
-        qtot, qmax = int(qcu_np[-1]), max(qlens)
-        qcu = torch.from_numpy(qcu_np).to(dev)
-        xq = synth.device_normal((qtot, QHID), seed=51)
-        qw = [torch.from_numpy(a).to(dev)
-              for a in synth.router_weights(np.random.default_rng(52), QHID, ROUTER_HIDDEN, QL)]
-        qroute = torch.empty((4, QL), dtype=torch.uint8, device=dev)
-        qlogits = torch.empty((4, QL), dtype=torch.float32, device=dev)
-        ws_q = torch.empty(_lib.fa_router_workspace_size(4, QHID, ROUTER_HIDDEN),
-                           dtype=torch.uint8, device=dev)
-        qsets = [(synth.device_normal((qtot, HQ, D), seed=60 + 3 * i),
-                  synth.device_normal((qtot, HKV, D), seed=61 + 3 * i),
-                  synth.device_normal((qtot, HKV, D), seed=62 + 3 * i)) for i in range(2)]
-        qo = torch.empty_like(qsets[0][0])
-
-        def qwen_prefill(all_fa):
-            a, b_ = ev(), ev()
-            a.record(stream)
-            _lib.fa_router_decide(xq, qcu, POOL, *qw, qroute, qlogits, ws_q)
-            r_np = np.ones((4, QL), np.uint8) if all_fa else qroute.cpu().numpy()
-            r_dev = torch.from_numpy(r_np).to(dev) if all_fa else qroute
-            for l in range(QL):
-                q_, k_, v_ = qsets[l % 2]
-                _lib.fa_attn_prefill(q_, k_, v_, qo, qcu, qmax, r_dev, l, QSINK, QWIN, QBLK,
-                                     scale, route_host=r_np)
-            b_.record(stream)
-            torch.cuda.synchronize()
-            return a.elapsed_time(b_), r_np
-
-        qwen_prefill(False)  # warm-up
-        ms_q, qr_np = qwen_prefill(False)
-        ms_q_fa, _ = qwen_prefill(True)
-        # decode: caches are prefix views of the per-layer decode buffers above
-        QC = qmax + 8
-        n_el = 4 * HKV * QC * D
-        qcl = torch.tensor([n + 1 for n in qlens], dtype=torch.int32, device=dev)
-        qd = synth.device_normal((4, HQ, D), seed=63)
-        qod = torch.empty_like(qd)
-        ws_qd = torch.empty(_lib.fa_decode_workspace_size(4, HQ, D, QC), dtype=torch.uint8,
-                            device=dev)
-        dec_ms = {}
-        for kind in ("routed", "all_fa"):
-            r_np = qr_np if kind == "routed" else np.ones((4, QL), np.uint8)
-            r_dev = torch.from_numpy(r_np).to(dev)
-            times = []
-            for rep in range(4):  # one warm-up step, the median of three
-                a, b_ = ev(), ev()
-                a.record(stream)
-                for l in range(QL):
-                    kc, vc = caches[l % len(caches)]
-                    _lib.fa_attn_decode(qd, qod, kc.view(-1)[:n_el].view(4, HKV, QC, D),
-                                        vc.view(-1)[:n_el].view(4, HKV, QC, D), qcl, r_dev, l,
-                                        QSINK, QWIN, QBLK, scale, workspace=ws_qd,
-                                        route_host=r_np)
-                b_.record(stream)
-                torch.cuda.synchronize()
-                if rep:
-                    times.append(a.elapsed_time(b_))
-            dec_ms[kind] = float(np.median(times))
-        qwen = {"layers": QL, "lengths": qlens, "sink": QSINK, "window": QWIN, "block": QBLK,
-                "fa_layers_per_seq": [int(x) for x in qr_np.sum(axis=1)],
-                "mixed_layers": int(((qr_np.sum(axis=0) > 0) & (qr_np.sum(axis=0) < 4)).sum()),
-                "prefill_tok_s": round(qtot / ms_q * 1e3, 1), "prefill_ms": round(ms_q, 3),
-                "all_fa_prefill_ms": round(ms_q_fa, 3),
-                "prefill_speedup_vs_all_fa": round(ms_q_fa / ms_q, 3),
-                "decode_tok_s": round(4 / dec_ms["routed"] * 1e3, 1),
-                "decode_ms_per_step": round(dec_ms["routed"], 3),
-                "all_fa_decode_ms": round(dec_ms["all_fa"], 3),
-                "decode_speedup_vs_all_fa": round(dec_ms["all_fa"] / dec_ms["routed"], 3)}
-        del xq, qsets, qo
+        qwen = qwen_leg(args, stream)
+        torch.cuda.empty_cache()
         log("qwen3-4b varlen leg done")
 
     # ---- roofline --------------------------------------------------------------
@@ -719,6 +748,7 @@ def main():
             "xattn_branch": xattn,
             "triangle_branch": tri,
             "qwen3_4b_varlen": qwen,
+            "single_layer_32k": config2,
         },
         "decode": {
             "tok_s": round(NB / t_decode, 1),
@@ -727,7 +757,7 @@ def main():
             "fa_layer_gbs": round(achieved_gbs, 1),
             "sa_layer_gbs": round(dec_sa_bytes / td_sa / 1e9, 1),
             "all_fa_ms": round(t_decode_allfa * 1e3, 4),
-            "speedup_vs_all_fa": round(t_decode_allfa / t_decode, 3),
+            "speedup_vs_all_fa": round(t_decode_allfa / t_decode_med, 3),
             "ring_cache_tok_s": round(NB / t_decode_ring, 1),
             "ring_cache_ms_per_token_step": round(t_decode_ring * 1e3, 4),
             "persistent_kv_gib_full": round(kv_full / 2**30, 3),
@@ -735,6 +765,7 @@ def main():
             "persistent_kv_saving": round(1 - kv_ring / kv_full, 4),
             "serving_sweep_32k": serving,
         },
+        "timing": timing,
         "roofline": {
             "kernel": "prefill_bf16_kernel<128> (FA layer, 131072 tokens)",
             "bound": "mfma", "achieved": round(achieved_tflops, 1),
@@ -754,12 +785,329 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity"] = cpu_baseline(
             args, sets[0], route_np, T, scale, t_prefill)
+        result["parity"]["needle"] = needle_parity(T, scale)
+        result["parity"]["pass"] = bool(result["parity"]["pass"]
+                                        and result["parity"]["needle"]["pass"])
     print(json.dumps(result))
 
 
+def _host_bits(t):
+    import numpy as np
+    import torch
+
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _f64(bits):
+    import numpy as np
+
+    from sparse_attention_layerrouter_amd import synth
+
+    return synth.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _parity_entry(o_gpu, o_ref, lse_gpu=None, l_ref=None):
+    """Max abs error, reference scale and relative error of one set of checked outputs."""
+    import numpy as np
+
+    err = float(np.abs(o_gpu - o_ref).max())
+    ref = float(np.abs(o_ref).max())
+    out = {"rows": int(o_ref.shape[0]), "max_abs_err": err, "max_abs_ref": ref,
+           "rel_err": err / ref if ref > 0 else None}
+    if lse_gpu is not None:
+        out["lse_max_abs_err"] = float(np.abs(lse_gpu - l_ref).max())
+    return out
+
+
+def _sa_row_pairs(rows, sink=SINK, window=WINDOW, block=BLOCK) -> int:
+    """Visible (row, key) pairs of the given SA rows (per head)."""
+    ns, nw = sink // block, window // block
+    n = 0
+    for t in rows:
+        i = int(t) // block
+        full = i if i < ns else ns + (i - max(ns, i - nw + 1))
+        n += full * block + (int(t) - i * block + 1)
+    return n
+
+
+def _time_calls(stream, fn, warmup, timed):
+    """HIP events around each of `timed` calls of fn after `warmup` untimed calls (ms)."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    evs = []
+    for _ in range(timed):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def config2_leg(stream, qkv):
+    """One Llama-shaped layer at 32768 tokens run as FA and as SA through the per-kind
+    kernels: 10 warm-up and 50 timed calls each (median / p10 / p90)."""
+    import numpy as np
+    import torch
+
+    from sparse_attention_layerrouter_amd import _lib
+
+    T2 = 32768
+    q, k, v = (x[:T2] for x in qkv)
+    dev = q.device
+    o = torch.empty_like(q)
+    cu = torch.tensor([0, T2], dtype=torch.int32, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    out = {"seq": T2, "sink": SINK, "window": WINDOW, "block": BLOCK}
+    for name, bit, pairs in (("fa", 1, pairs_fa(T2)), ("sa", 0, pairs_sa(T2))):
+        r = np.array([[bit]], np.uint8)
+        r_dev = torch.from_numpy(r).to(dev)
+
+        def call():
+            _lib.fa_attn_prefill(q, k, v, o, cu, T2, r_dev, 0, SINK, WINDOW, BLOCK, scale,
+                                 route_host=r)
+
+        ms = _time_calls(stream, call, 10, 50)
+        med = float(np.median(ms))
+        fl = flops_of_pairs(pairs)
+        out[name] = {"ms": dist(ms), "tok_s": round(T2 / med * 1e3, 1),
+                     "algorithmic_flop": fl, "tflops": round(fl / (med * 1e-3) / 1e12, 1),
+                     "mfma_frac": round(fl / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    out["fa_over_sa"] = round(out["fa"]["ms"]["median"] / out["sa"]["ms"]["median"], 3)
+    return out
+
+
+def qwen_leg(args, stream):
+    """Qwen3-4B-shaped mixed workload: 36 layers, a varlen batch of 4 sequences
+    (16384 / 32768 / 49152 / 65536 tokens), a 2560 -> 256 -> 36 router giving
+    per-sequence masks (FA and SA sequences share a launch where their bits differ),
+    SA sink 128 / window 4096 / block 128.  The routed prefill and its all-FA
+    reference; then each layer's KV cache is filled from that layer's prefill K/V,
+    and a loop of decode steps appends one token per sequence and step (the cache
+    grows from T_b + 1 to T_b + steps tokens; decode reuses the router's mask), run
+    routed and all-FA over the same caches.  The last step's outputs are checked
+    against the oracle on the grown caches."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from sparse_attention_layerrouter_amd import _lib, synth
+
+    dev = torch.device("cuda:0")
+    scale = 1.0 / math.sqrt(D)
+    QL, QHID, QSINK, QWIN, QBLK = 36, 2560, 128, 4096, 128
+    qlens = [16384, 32768, 49152, 65536]
+    NS = args.qwen_steps
+    qcu_np = synth.cu_seqlens_of(qlens)
+    qtot, qmax = int(qcu_np[-1]), max(qlens)
+    qcu = torch.from_numpy(qcu_np).to(dev)
+    xq = synth.device_normal((qtot, QHID), seed=51)
+    qw = [torch.from_numpy(a).to(dev)
+          for a in synth.router_weights(np.random.default_rng(52), QHID, ROUTER_HIDDEN, QL)]
+    qroute = torch.empty((4, QL), dtype=torch.uint8, device=dev)
+    qlogits = torch.empty((4, QL), dtype=torch.float32, device=dev)
+    ws_q = torch.empty(_lib.fa_router_workspace_size(4, QHID, ROUTER_HIDDEN), dtype=torch.uint8,
+                       device=dev)
+    qsets = [(synth.device_normal((qtot, HQ, D), seed=60 + 3 * i),
+              synth.device_normal((qtot, HKV, D), seed=61 + 3 * i),
+              synth.device_normal((qtot, HKV, D), seed=62 + 3 * i)) for i in range(2)]
+    qo = torch.empty_like(qsets[0][0])
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def qwen_prefill(all_fa):
+        a, b_ = ev(), ev()
+        a.record(stream)
+        _lib.fa_router_decide(xq, qcu, POOL, *qw, qroute, qlogits, ws_q)
+        r_np = np.ones((4, QL), np.uint8) if all_fa else qroute.cpu().numpy()
+        r_dev = torch.from_numpy(r_np).to(dev) if all_fa else qroute
+        for l in range(QL):
+            q_, k_, v_ = qsets[l % 2]
+            _lib.fa_attn_prefill(q_, k_, v_, qo, qcu, qmax, r_dev, l, QSINK, QWIN, QBLK,
+                                 scale, route_host=r_np)
+        b_.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b_), r_np
+
+    qwen_prefill(False)  # warm-up
+    pre_ms, fa_ms = [], []
+    for _ in range(3):
+        ms, qr_np = qwen_prefill(False)
+        pre_ms.append(ms)
+    for _ in range(2):
+        fa_ms.append(qwen_prefill(True)[0])
+    del xq, qo
+    log("qwen prefill timed")
+
+    # ---- per-layer KV caches [4][8][T_b + steps][128], holding each layer's prefill K/V
+    QC = qmax + NS
+    caches = []
+    for l in range(QL):
+        _, k_, v_ = qsets[l % 2]
+        kc = torch.empty((4, HKV, QC, D), dtype=torch.bfloat16, device=dev)
+        vc = torch.empty_like(kc)
+        for b in range(4):
+            s, e = int(qcu_np[b]), int(qcu_np[b + 1])
+            kc[b, :, :e - s] = k_[s:e].transpose(0, 1)
+            vc[b, :, :e - s] = v_[s:e].transpose(0, 1)
+        caches.append((kc, vc))
+    del qsets
+    torch.cuda.empty_cache()
+    # per step and layer: a query, and the new token's K and V (appended by the call)
+    qd_all = synth.device_normal((NS, QL, 4, HQ, D), seed=64)
+    kn_all = synth.device_normal((NS, QL, 4, HKV, D), seed=65)
+    vn_all = synth.device_normal((NS, QL, 4, HKV, D), seed=66)
+    # the last step's queries point at one prefill key each, so its outputs are O(1)
+    for l in range(QL):
+        qd_all[NS - 1, l] = synth.device_needle_decode_q(caches[l][0], HQ, qlens, seed=700 + l)[0]
+    cl0 = torch.tensor([n + 1 for n in qlens], dtype=torch.int32, device=dev)
+    cl = cl0.clone()
+    o_last = torch.empty((QL, 4, HQ, D), dtype=torch.bfloat16, device=dev)
+    lse_last = torch.empty((QL, 4, HQ), dtype=torch.float32, device=dev)
+    ws_qd = torch.empty(_lib.fa_decode_workspace_size(4, HQ, D, QC), dtype=torch.uint8,
+                        device=dev)
+    torch.cuda.synchronize()
+    log(f"qwen decode caches resident ({QL} layers x 4 x {QC} tokens)")
+
+    def decode_loop(r_np, n_steps):
+        """n_steps appending decode steps from cache length T_b + 1; per-step ms."""
+        r_dev = torch.from_numpy(r_np).to(dev)
+        cl.copy_(cl0)
+        evs = []
+        for j in range(n_steps):
+            a, b_ = ev(), ev()
+            a.record(stream)
+            for l in range(QL):
+                kc, vc = caches[l]
+                _lib.fa_attn_decode(qd_all[j, l], o_last[l], kc, vc, cl, r_dev, l, QSINK, QWIN,
+                                    QBLK, scale, workspace=ws_qd, k_new=kn_all[j, l],
+                                    v_new=vn_all[j, l], lse=lse_last[l], route_host=r_np)
+            b_.record(stream)
+            cl.add_(1)  # the cache grows by the appended token
+            evs.append((a, b_))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
+
+    decode_loop(qr_np, 2)  # warm-up: writes the same tokens as the first two steps below
+    routed_ms = decode_loop(qr_np, NS)
+    final = [n + NS for n in qlens]
+    o_fin, lse_fin = o_last.clone(), lse_last.clone()
+    allfa_np = np.ones((4, QL), np.uint8)
+    allfa_ms = decode_loop(allfa_np, NS)
+    log("qwen decode loops timed")
+
+    # ---- the last routed step against the oracle on the grown caches: a layer with
+    # mixed routes, an all-FA and an all-SA layer (when the mask has them), KV heads 0, 7
+    G = HQ // HKV
+    n_fa = qr_np.sum(axis=0)
+    picks = {}
+    for kind, sel in (("mixed", (n_fa > 0) & (n_fa < 4)), ("fa", n_fa == 4), ("sa", n_fa == 0)):
+        idx = np.nonzero(sel)[0]
+        if idx.size:
+            picks[kind] = int(idx[0])
+    checks = {}
+    ok = True
+    for kind, l in picks.items():
+        kc, vc = caches[l]
+        errs, lerrs, refs = [], [], []
+        for g in (0, HKV - 1):
+            o_ref, l_ref = oracle.attn_decode(
+                _host_bits(qd_all[NS - 1, l][:, g * G:(g + 1) * G]), _host_bits(kc[:, g:g + 1]),
+                _host_bits(vc[:, g:g + 1]), final, qr_np, l, QSINK, QWIN, QBLK, scale)
+            og = _f64(_host_bits(o_fin[l][:, g * G:(g + 1) * G]))
+            errs.append(float(np.abs(og - o_ref).max()))
+            lerrs.append(float(np.abs(lse_fin[l][:, g * G:(g + 1) * G].cpu().numpy()
+                                      - l_ref).max()))
+            refs.append(float(np.abs(o_ref).max()))
+        checks[kind] = {"layer": l, "max_abs_err": max(errs), "lse_max_abs_err": max(lerrs),
+                        "max_abs_ref": max(refs)}
+        ok = ok and max(errs) <= 2e-2 and max(lerrs) <= 1e-3
+    # appended tokens landed at their positions (the last one of each sequence)
+    for b in range(4):
+        kc, _ = caches[picks.get("mixed", 0)]
+        ok = ok and torch.equal(kc[b, :, final[b] - 1], kn_all[NS - 1, picks.get("mixed", 0), b])
+
+    # algorithmic bytes of the routed loop: the kept K/V rows of every step
+    def kept(n, fa):
+        return kept_tokens_decode(n, fa, QSINK, QWIN, QBLK)
+
+    loop_bytes = 0
+    for j in range(NS):
+        for b in range(4):
+            n = qlens[b] + 1 + j
+            for l in range(QL):
+                loop_bytes += kept(n, bool(qr_np[b, l])) * HKV * D * 4
+    t_routed, t_allfa = sum(routed_ms) * 1e-3, sum(allfa_ms) * 1e-3
+    out = {
+        "layers": QL, "lengths": qlens, "sink": QSINK, "window": QWIN, "block": QBLK,
+        "fa_layers_per_seq": [int(x) for x in qr_np.sum(axis=1)],
+        "mixed_layers": int(((n_fa > 0) & (n_fa < 4)).sum()),
+        "prefill_tok_s": round(qtot / float(np.median(pre_ms)) * 1e3, 1),
+        "prefill_ms": dist(pre_ms), "all_fa_prefill_ms": dist(fa_ms),
+        "prefill_speedup_vs_all_fa": round(float(np.median(fa_ms) / np.median(pre_ms)), 3),
+        "decode": {
+            "steps_per_seq": NS, "cache_len_first": [n + 1 for n in qlens], "cache_len_last": final,
+            "tok_s": round(4 * NS / t_routed, 1),
+            "step_ms": dist(routed_ms),
+            "all_fa_tok_s": round(4 * NS / t_allfa, 1),
+            "all_fa_step_ms": dist(allfa_ms),
+            "speedup_vs_all_fa": round(t_allfa / t_routed, 3),
+            "algorithmic_bytes": loop_bytes,
+            "achieved_gbs": round(loop_bytes / t_routed / 1e9, 1),
+            "parity_last_step": checks, "parity_pass": bool(ok),
+        },
+    }
+    del caches, qd_all, kn_all, vn_all
+    return out
+
+
+def needle_parity(T, scale):
+    """FA and SA prefill at T on needle inputs (every query row a copy of one earlier
+    key, so outputs are O(1)) through the per-kind kernels, sampled rows against the
+    oracle: the check a dropped or mis-read tile cannot pass."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from sparse_attention_layerrouter_amd import _lib, synth
+
+    dev = torch.device("cuda:0")
+    q, k, v, _ = synth.device_needle_qkv(T, HQ, HKV, D, seed=301)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    qh, kh, vh = _host_bits(q), _host_bits(k), _host_bits(v)
+    out, ok = {}, True
+    for name, bit, n_rand in (("fa", 1, 10), ("sa", 0, 96)):
+        o = torch.empty_like(q)
+        lse = torch.empty((T, HQ), dtype=torch.float32, device=dev)
+        r = np.array([[bit]], np.uint8)
+        _lib.fa_attn_prefill(q, k, v, o, cu, T, torch.from_numpy(r).to(dev), 0, SINK, WINDOW,
+                             BLOCK, scale, lse=lse, route_host=r)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(40 + bit)
+        rows = np.array(sorted({0, T // 2, T - 2, T - 1}
+                               | set(rng.integers(0, T, n_rand).tolist())), np.int32)
+        o_ref, l_ref = oracle.attn_prefill(qh, kh, vh, [0, T], r, 0, SINK, WINDOW, BLOCK, scale,
+                                           rows=rows)
+        e = _parity_entry(_f64(_host_bits(o)[rows]), o_ref, lse.cpu().numpy()[rows], l_ref)
+        heads = slice(None) if bit else slice(1, None, 2)
+        e["min_row_max_abs_ref"] = float(np.abs(o_ref[:, heads]).max(axis=(1, 2)).min())
+        ok = ok and e["max_abs_err"] <= 2e-2 and e["lse_max_abs_err"] <= 1e-3 \
+            and e["min_row_max_abs_ref"] >= 0.1
+        out[name] = e
+    out["inputs"] = ("needle: query row t of head h = 2 K[g][h/4], g drawn in [0, t] (even "
+                     "heads) or among the first 128 / last 64 positions (odd heads, kept by SA)")
+    out["pass"] = bool(ok)
+    return out
+
+
 def cpu_baseline(args, qkv, route_np, T, scale, t_prefill_gpu):
-    """Time the oracle on a bounded sample of the same prefill workload and scale it to
-    the metric's unit by visible-pair count.  Also compares the sampled GPU rows."""
+    """Time the oracle on a bounded sample of the same prefill workload, on every core
+    the process may use and on one core, and scale each to the metric's unit by
+    visible-pair count.  The sampled GPU rows are compared per layer kind."""
     import numpy as np
     import torch
 
@@ -769,56 +1117,184 @@ def cpu_baseline(args, qkv, route_np, T, scale, t_prefill_gpu):
     q, k, v = qkv
     dev = q.device
     cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
-    out = {}
-    errs = []
-    cores = os.cpu_count() or 1
-    samples = {}
+    model, cores = cpu_info()
+    qh, kh, vh = _host_bits(q), _host_bits(k), _host_bits(v)
+    samples, kinds = {}, {}
     for name, bit, n_rows in (("fa", 1, args.cpu_rows), ("sa", 0, 4 * args.cpu_rows)):
         o = torch.empty_like(q)
-        _lib.fa_attn_prefill(q, k, v, o, cu, T,
-                             torch.tensor([[bit]], dtype=torch.uint8, device=dev), 0, SINK,
-                             WINDOW, BLOCK, scale, route_host=np.array([[bit]], np.uint8))
+        lse = torch.empty((T, HQ), dtype=torch.float32, device=dev)
+        r = np.array([[bit]], np.uint8)
+        _lib.fa_attn_prefill(q, k, v, o, cu, T, torch.from_numpy(r).to(dev), 0, SINK, WINDOW,
+                             BLOCK, scale, lse=lse, route_host=r)
         torch.cuda.synchronize()
         rng = np.random.default_rng(5 + bit)
         rows = np.sort(rng.choice(T, size=n_rows, replace=False)).astype(np.int32)
-        qh = q.view(torch.int16).cpu().numpy().view(np.uint16)
-        kh = k.view(torch.int16).cpu().numpy().view(np.uint16)
-        vh = v.view(torch.int16).cpu().numpy().view(np.uint16)
         t0 = time.perf_counter()
-        o_ref, _ = oracle.attn_prefill(qh, kh, vh, [0, T], np.array([[bit]], np.uint8), 0,
-                                       SINK, WINDOW, BLOCK, scale, rows=rows, n_threads=cores)
+        o_ref, l_ref = oracle.attn_prefill(qh, kh, vh, [0, T], r, 0, SINK, WINDOW, BLOCK, scale,
+                                           rows=rows, n_threads=cores)
         dt = time.perf_counter() - t0
         log(f"oracle {name}: {len(rows)} rows in {dt:.1f} s on {cores} threads")
-        # visible pairs of the sampled rows (per head)
-        if bit:
-            sp = int((rows + 1).sum())
-        else:
-            sp = 0
-            for t in rows:
-                i = t // BLOCK
-                full = i if i < SINK // BLOCK else SINK // BLOCK + (
-                    i - max(SINK // BLOCK, i - WINDOW // BLOCK + 1))
-                sp += full * BLOCK + (t - i * BLOCK + 1)
-        total_pairs = pairs_fa(T) if bit else pairs_sa(T)
-        samples[name] = (dt, sp, total_pairs, len(rows))
-        og = o[torch.from_numpy(rows.astype(np.int64)).to(dev)].float().cpu().numpy()
-        errs.append(float(np.abs(og - o_ref).max()))
+        sp = int((rows + 1).sum()) if bit else _sa_row_pairs(rows)
+        samples[name] = (dt, sp, pairs_fa(T) if bit else pairs_sa(T), len(rows))
+        kinds[name] = _parity_entry(_f64(_host_bits(o)[rows]), o_ref, lse.cpu().numpy()[rows],
+                                    l_ref)
+    # one core, smaller samples
+    one = {}
+    for name, bit, n_rows in (("fa", 1, max(2, args.cpu_rows // 32)),
+                              ("sa", 0, max(8, args.cpu_rows // 8))):
+        rng = np.random.default_rng(8 + bit)
+        rows = np.sort(rng.choice(T, size=n_rows, replace=False)).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.attn_prefill(qh, kh, vh, [0, T], np.array([[bit]], np.uint8), 0, SINK, WINDOW,
+                            BLOCK, scale, rows=rows, n_threads=1)
+        dt = time.perf_counter() - t0
+        sp = int((rows + 1).sum()) if bit else _sa_row_pairs(rows)
+        one[name] = (dt, sp, len(rows))
+    log(f"oracle one core: {one['fa'][0]:.1f} s + {one['sa'][0]:.1f} s")
     n_fa = int(route_np.sum())
-    t_fa_cpu = samples["fa"][0] * samples["fa"][2] / samples["fa"][1]
-    t_sa_cpu = samples["sa"][0] * samples["sa"][2] / samples["sa"][1]
-    t_cpu = n_fa * t_fa_cpu + (N_LAYERS - n_fa) * t_sa_cpu
+    n_sa = N_LAYERS - n_fa
+
+    def scaled(fa, sa):  # seconds for the routed 32-layer prefill
+        return (n_fa * fa[0] * pairs_fa(T) / fa[1] + n_sa * sa[0] * pairs_sa(T) / sa[1])
+
+    t_cpu = scaled(samples["fa"][:2], samples["sa"][:2])
+    t_cpu1 = scaled(one["fa"][:2], one["sa"][:2])
     out = {
         "value": round(T / t_cpu, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
-        "sample": (f"oracle (fp64, threads={cores}) on {samples['fa'][3]} random query rows x 32 "
-                   f"heads of one FA layer ({samples['fa'][0]:.1f} s) and {samples['sa'][3]} "
-                   f"rows of one SA layer ({samples['sa'][0]:.1f} s) at {T} tokens, scaled by "
-                   f"visible-pair count to the routed 32-layer prefill ({n_fa} FA layers); "
-                   f"router time ignored"),
+        "cpu_model": model,
+        "sample": (f"oracle (fp64 sums, {cores} threads) on {samples['fa'][3]} random query rows "
+                   f"x 32 heads of one FA layer ({samples['fa'][0]:.1f} s) and "
+                   f"{samples['sa'][3]} rows of one SA layer ({samples['sa'][0]:.1f} s) at {T} "
+                   f"tokens, extrapolated by visible-pair count to the routed 32-layer prefill "
+                   f"({n_fa} FA layers); router time ignored"),
+        "value_1core": round(T / t_cpu1, 5),
+        "sample_1core": (f"{one['fa'][2]} FA rows ({one['fa'][0]:.1f} s) and {one['sa'][2]} SA "
+                         f"rows ({one['sa'][0]:.1f} s) on one thread, extrapolated the same way"),
         "gpu_over_cpu": round(t_cpu / t_prefill_gpu, 1),
     }
-    parity = {"sampled_rows_max_abs_err": max(errs), "tolerance": 2e-2,
-              "pass": max(errs) <= 2e-2}
+    ok = all(kinds[n]["max_abs_err"] <= 2e-2 and kinds[n]["lse_max_abs_err"] <= 1e-3
+             for n in kinds)
+    parity = {"workload_rows": kinds, "tolerance": 2e-2, "lse_tolerance": 1e-3, "pass": ok,
+              "note": ("workload rows are i.i.d. N(0,1): late FA rows have |O| ~ sqrt(e/T), "
+                       "so max_abs_ref shows how much the bar can see; the needle rows below "
+                       "have O(1) outputs")}
     return out, parity
+
+
+def cpu_full(stream):
+    """Unsampled oracle runs, timed on every core the process may use, with full-row
+    parity of the same GPU launches: the tiny two-layer case (router + FA + SA, fp32),
+    one SA layer at 32768 tokens (Llama shape, bf16; an FA layer at that size is
+    sampled and extrapolated), and one FA and one SA decode layer at batch 8 over
+    131072-token caches (every head)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from sparse_attention_layerrouter_amd import _lib, synth
+
+    dev = torch.device("cuda:0")
+    model, cores = cpu_info()
+    out = {"cpu_model": model, "cores": cores}
+
+    # ---- the tiny case, every output
+    c = synth.tiny_case(0)
+    cfg = c["cfg"]
+    cu_np = c["cu_seqlens"]
+    cu = torch.from_numpy(cu_np).to(dev)
+    route = torch.zeros((1, 2), dtype=torch.uint8, device=dev)
+    logits = torch.zeros((1, 2), dtype=torch.float32, device=dev)
+    _lib.fa_router_decide(torch.from_numpy(c["x_q"]).to(dev), cu, cfg["pool"],
+                          *(torch.from_numpy(c[n]).to(dev) for n in ("w1", "b1", "w2", "b2")),
+                          route, logits)
+    sc = 1 / math.sqrt(cfg["d"])
+    og, lg = [], []
+    for layer, (q, k, v) in enumerate(c["layers"]):
+        o = torch.empty((cfg["seq"], cfg["hq"], cfg["d"]), dtype=torch.float32, device=dev)
+        lse = torch.empty((cfg["seq"], cfg["hq"]), dtype=torch.float32, device=dev)
+        _lib.fa_attn_prefill(*(torch.from_numpy(x).to(dev) for x in (q, k, v)), o, cu,
+                             cfg["seq"], route, layer, cfg["sink"], cfg["window"], cfg["block"],
+                             sc, lse=lse)
+        og.append(o)
+        lg.append(lse)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    r_ref, _, _ = oracle.router(c["x_q"], cu_np, cfg["pool"], c["w1"], c["b1"], c["w2"], c["b2"])
+    refs = [oracle.attn_prefill(q, k, v, cu_np, r_ref, layer, cfg["sink"], cfg["window"],
+                                cfg["block"], sc, n_threads=cores)
+            for layer, (q, k, v) in enumerate(c["layers"])]
+    dt = time.perf_counter() - t0
+    out["tiny_case"] = {
+        "kind": "full", "seconds": round(dt, 4),
+        "route_bits_equal": bool(np.array_equal(route.cpu().numpy(), r_ref)),
+        "layers": [_parity_entry(og[i].cpu().numpy().astype(np.float64), refs[i][0],
+                                 lg[i].cpu().numpy(), refs[i][1]) for i in range(2)],
+        "tolerance": 1e-4}
+    log("cpu-full: tiny case done")
+
+    # ---- one SA layer at 32768 tokens (every row), one FA layer sampled
+    T2 = 32768
+    q = synth.device_normal((T2, HQ, D), seed=0)
+    k = synth.device_normal((T2, HKV, D), seed=1)
+    v = synth.device_normal((T2, HKV, D), seed=2)
+    qh, kh, vh = _host_bits(q), _host_bits(k), _host_bits(v)
+    cu2 = torch.tensor([0, T2], dtype=torch.int32, device=dev)
+    sc = 1 / math.sqrt(D)
+    for name, bit in (("sa_layer_32k", 0), ("fa_layer_32k", 1)):
+        r = np.array([[bit]], np.uint8)
+        o = torch.empty_like(q)
+        lse = torch.empty((T2, HQ), dtype=torch.float32, device=dev)
+        gpu_ms = _time_calls(stream, lambda: _lib.fa_attn_prefill(
+            q, k, v, o, cu2, T2, torch.from_numpy(r).to(dev), 0, SINK, WINDOW, BLOCK, sc,
+            lse=lse, route_host=r), 2, 5)
+        rows = None if not bit else np.sort(
+            np.random.default_rng(3).choice(T2, 512, replace=False)).astype(np.int32)
+        t0 = time.perf_counter()
+        o_ref, l_ref = oracle.attn_prefill(qh, kh, vh, [0, T2], r, 0, SINK, WINDOW, BLOCK, sc,
+                                           rows=rows, n_threads=cores)
+        dt = time.perf_counter() - t0
+        sel = np.arange(T2) if rows is None else rows
+        e = _parity_entry(_f64(_host_bits(o)[sel]), o_ref, lse.cpu().numpy()[sel], l_ref)
+        pairs = pairs_sa(T2) if not bit else pairs_fa(T2)
+        done = _sa_row_pairs(sel) if not bit else int((sel + 1).sum())
+        out[name] = {"kind": "full" if rows is None else "extrapolated",
+                     "rows": int(sel.size), "seconds": round(dt, 3),
+                     "seconds_full_layer": round(dt * pairs / done, 2),
+                     "gpu_ms": dist(gpu_ms),
+                     "cpu_over_gpu": round(dt * pairs / done / (np.median(gpu_ms) * 1e-3), 1),
+                     "parity": e}
+        log(f"cpu-full: {name} {dt:.1f} s")
+    del q, k, v, o
+
+    # ---- one FA and one SA decode layer at batch 8 over 131072-token caches, every head
+    B, n = 8, 131072
+    kc = torch.empty((B, HKV, n, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    for b in range(B):
+        kc[b] = synth.device_normal((HKV, n, D), seed=1000 + 2 * b)
+        vc[b] = synth.device_normal((HKV, n, D), seed=1001 + 2 * b)
+    qd = synth.device_normal((B, HQ, D), seed=7)
+    cl = torch.full((B,), n, dtype=torch.int32, device=dev)
+    r = np.array([[1, 0]] * B, np.uint8)
+    rd = torch.from_numpy(r).to(dev)
+    ws = torch.empty(_lib.fa_decode_workspace_size(B, HQ, D, n), dtype=torch.uint8, device=dev)
+    kch, vch, qdh = _host_bits(kc), _host_bits(vc), _host_bits(qd)
+    for name, layer in (("decode_fa_layer_b8_131k", 0), ("decode_sa_layer_b8_131k", 1)):
+        o = torch.empty_like(qd)
+        lse = torch.empty((B, HQ), dtype=torch.float32, device=dev)
+        gpu_ms = _time_calls(stream, lambda: _lib.fa_attn_decode(
+            qd, o, kc, vc, cl, rd, layer, SINK, WINDOW, BLOCK, sc, lse=lse, route_host=r,
+            workspace=ws), 5, 20)
+        t0 = time.perf_counter()
+        o_ref, l_ref = oracle.attn_decode(qdh, kch, vch, [n] * B, r, layer, SINK, WINDOW, BLOCK,
+                                          sc, n_threads=cores)
+        dt = time.perf_counter() - t0
+        out[name] = {"kind": "full", "seconds": round(dt, 3), "gpu_ms": dist(gpu_ms),
+                     "cpu_over_gpu": round(dt / (np.median(gpu_ms) * 1e-3), 1),
+                     "parity": _parity_entry(_f64(_host_bits(o)), o_ref, lse.cpu().numpy(),
+                                             l_ref)}
+        log(f"cpu-full: {name} {dt:.1f} s")
+    return out
 
 
 if __name__ == "__main__":

@@ -8,6 +8,13 @@
         HBM bytes per launch of the hot kernels from FETCH_SIZE / WRITE_SIZE
         passes (KiB per dispatch), each scaled by what the same counter reads
         for a plain 1 GiB read + 1 GiB write elementwise kernel.
+    python -m sparse_attention_layerrouter_amd.rocprof_summary mfma DIR PROFILE_JSON OUT_JSON
+        matrix-core evidence of the hot kernels from one counter pass with
+        SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE
+        and SQ_BUSY_CU_CYCLES (plus --kernel-trace for durations): executed MFMA
+        flops (MOPS x 512) against the algorithmic flops bench.py --profile
+        printed (PROFILE_JSON), the share of SIMD cycles the matrix cores were
+        busy, and the clock the kernel ran at.
 """
 from __future__ import annotations
 
@@ -98,11 +105,78 @@ def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_json):
     return out
 
 
+# SIMDs of an MI355X (256 CUs x 4) and XCDs; GRBM_GUI_ACTIVE is reported summed over
+# the 8 XCDs, each of which counts the same active cycles
+N_SIMD = 1024
+N_XCD = 8
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE",
+                 "SQ_BUSY_CU_CYCLES")
+
+
+def _durations(directory):
+    """{dispatch id: duration ns} from the kernel trace written beside the counters."""
+    out = {}
+    for r in _rows(directory, "kernel_trace.csv"):
+        did = r.get("Dispatch_Id")
+        if did is None:
+            continue
+        out[did] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    return out
+
+
+def mfma(directory, profile_json, out_json):
+    with open(profile_json) as f:
+        prof = json.load(f)
+    alg = prof.get("algorithmic", {})
+    dur = _durations(directory)
+    per = {}  # kernel key -> dispatch -> {counter: value}
+    for r in _rows(directory, "counter_collection.csv"):
+        cname = r.get("Counter_Name")
+        if cname not in MFMA_COUNTERS:
+            continue
+        for key, (needle, _) in HOT_KERNELS.items():
+            if needle in r["Kernel_Name"]:
+                d = per.setdefault(key, {}).setdefault(r["Dispatch_Id"], {})
+                d[cname] = d.get(cname, 0.0) + float(r["Counter_Value"])
+    out = {"_note": ("per kernel: mean over its dispatches. executed_flop = MOPS_BF16 x 512; "
+                     "mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 "
+                     "SIMDs), the MfmaUtil expression; clock = GRBM_GUI_ACTIVE / 8 / kernel "
+                     "duration; cu_busy = SQ_BUSY_CU_CYCLES x 4 / (GRBM_GUI_ACTIVE / 8 x 256)"),
+           "_workload": {k: v for k, v in prof.items() if k != "algorithmic"}}
+    for key, dispatches in per.items():
+        n = len(dispatches)
+        mean = {c: sum(d.get(c, 0.0) for d in dispatches.values()) / n for c in MFMA_COUNTERS}
+        durs = [dur[i] for i in dispatches if i in dur]
+        dns = sum(durs) / len(durs) if durs else None
+        gui = mean["GRBM_GUI_ACTIVE"] / N_XCD
+        e = {"kernel": HOT_KERNELS[key][0], "dispatches": n, "counters_mean": mean,
+             "duration_us": dns / 1e3 if dns else None,
+             "executed_flop": mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0,
+             "mfma_busy": mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * N_SIMD) if gui else None,
+             "cu_busy": mean["SQ_BUSY_CU_CYCLES"] * 4.0 / (gui * 256) if gui else None,
+             "clock_ghz": gui / dns if dns else None}
+        a = alg.get(key, {}).get("flop")
+        if a:
+            e["algorithmic_flop"] = a
+            e["executed_over_algorithmic"] = e["executed_flop"] / a
+            if dns:
+                e["algorithmic_tflops"] = a / dns / 1e3
+                # the same rate against the peak at the clock the kernel ran at
+                e["peak_at_clock_tflops"] = 256 * 4096 * e["clock_ghz"] * 1e9 / 1e12
+        e["source_hash"] = source_hash(*HOT_KERNELS[key][1])
+        out[key] = e
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 3 and sys.argv[1] == "stats":
         print(stats(sys.argv[2]))
     elif len(sys.argv) == 7 and sys.argv[1] == "traffic":
         print(json.dumps(traffic(*sys.argv[2:7]), indent=1))
+    elif len(sys.argv) == 5 and sys.argv[1] == "mfma":
+        print(json.dumps(mfma(*sys.argv[2:5]), indent=1))
     else:
         print(__doc__)
         sys.exit(2)
