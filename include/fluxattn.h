@@ -381,6 +381,34 @@ fa_status fa_attn_decode(const void *q, void *o, float *lse, const void *k_new,
                          float sm_scale, void *workspace, size_t ws_bytes,
                          void *stream);
 
+/*
+ * fa_attn_decode_noalloc -- fa_attn_decode for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, kernels, results
+ * (bit for bit) and device behaviour as fa_attn_decode, without workspace and
+ * ws_bytes: the split partials go to a static device array of the library,
+ * 64 MiB per GPU it runs on, held until the process ends.  The call allocates
+ * nothing.  Its first call on a device looks up that device's copy of the array
+ * (with the device current); the stream must belong to the current device.
+ * Calls that overlap on one GPU share the array and race: serialise them (one
+ * stream, or events).
+ * Errors: as fa_attn_decode; partials larger than the array (batch x n_q_heads
+ * x splits x (head_dim + 1) x 4 bytes above 64 MiB, e.g. batch 64 with 32 heads,
+ * head_dim 128 and 64 splits of a long cache) -> FA_ERR_WORKSPACE; a stream of
+ * another device -> FA_ERR_HIP.
+ */
+fa_status fa_attn_decode_noalloc(const void *q, void *o, float *lse,
+                                 const void *k_new, const void *v_new,
+                                 void *k_cache, void *v_cache, int32_t max_cache,
+                                 const int32_t *cache_len, int32_t dtype,
+                                 int32_t batch, int32_t n_q_heads,
+                                 int32_t n_kv_heads, int32_t head_dim,
+                                 const uint8_t *route, const uint8_t *route_host,
+                                 int32_t n_layers, int32_t layer,
+                                 int32_t sink_tokens, int32_t window_tokens,
+                                 int32_t block_tokens, float sm_scale,
+                                 void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Compact KV cache for SA layers                                           */
 /* ------------------------------------------------------------------------ */

@@ -24,7 +24,7 @@ EXPORTS = (
     "fa_block_plan", "fa_attn_prefill", "fa_decode_workspace_size", "fa_attn_decode",
     "fa_kv_compact", "fa_attn_decode_ring", "fa_attn_prefill_kv", "fa_xattn_scores",
     "fa_xattn_select", "fa_attn_prefill_xattn", "fa_attn_prefill_triangle",
-    "fa_xattn_workspace_size",
+    "fa_xattn_workspace_size", "fa_attn_decode_noalloc",
 )
 
 
@@ -81,6 +81,9 @@ def lib() -> ctypes.CDLL:
     L.fa_attn_decode.restype = I32
     L.fa_attn_decode.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, P, P, I32,
                                  I32, I32, I32, I32, F, P, SZ, P]
+    L.fa_attn_decode_noalloc.restype = I32
+    L.fa_attn_decode_noalloc.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32,
+                                         P, P, I32, I32, I32, I32, I32, F, P]
     L.fa_kv_compact.restype = I32
     L.fa_kv_compact.argtypes = [P, P, I32, P, I32, I32, I32, I32, I32, I32, P, P, I32, P]
     L.fa_attn_decode_ring.restype = I32
@@ -293,6 +296,23 @@ def fa_attn_decode(q, o, k_cache, v_cache, cache_len, route, layer, sink_tokens,
         max_cache, _ptr(cache_len), _dtype_code(q), batch, hq, hkv, d, _ptr(route), rh,
         route.shape[1], layer, sink_tokens, window_tokens, block_tokens, float(sm_scale),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    del keep
+
+
+def fa_attn_decode_noalloc(q, o, k_cache, v_cache, cache_len, route, layer, sink_tokens,
+                           window_tokens, block_tokens, sm_scale, k_new=None, v_new=None,
+                           lse=None, route_host=None, stream=None):
+    """fa_attn_decode with the split partials in the library's static device scratch
+    (no workspace, nothing allocated)."""
+    _require_cuda(q, o, k_cache, v_cache, cache_len, route, k_new, v_new, lse)
+    batch, hq, d = q.shape
+    hkv, max_cache = k_cache.shape[1], k_cache.shape[2]
+    keep, rh = _host_u8(route_host)
+    _check(lib().fa_attn_decode_noalloc(
+        _ptr(q), _ptr(o), _ptr(lse), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        max_cache, _ptr(cache_len), _dtype_code(q), batch, hq, hkv, d, _ptr(route), rh,
+        route.shape[1], layer, sink_tokens, window_tokens, block_tokens, float(sm_scale),
+        _stream(stream)))
     del keep
 
 

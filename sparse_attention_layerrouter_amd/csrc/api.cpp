@@ -143,7 +143,7 @@ extern "C" {
 
 const char *fa_last_error(void) { return g_last_error.c_str(); }
 
-int32_t fa_abi_version(void) { return 7; }
+int32_t fa_abi_version(void) { return 8; }
 
 size_t fa_router_workspace_size(int32_t batch, int32_t hidden, int32_t router_hidden)
 {
@@ -420,7 +420,7 @@ size_t fa_decode_workspace_size(int32_t batch, int32_t n_q_heads, int32_t head_d
 
 namespace {
 
-fa_status decode_impl(const char *fn, bool ring, const void *q, void *o, float *lse,
+fa_status decode_impl(const char *fn, bool ring, bool noalloc, const void *q, void *o, float *lse,
                       const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                       int32_t max_cache, const int32_t *cache_len, int32_t dtype, int32_t batch,
                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
@@ -471,7 +471,12 @@ fa_status decode_impl(const char *fn, bool ring, const void *q, void *o, float *
     const size_t rows = (size_t)batch * n_q_heads * a.n_splits;
     const size_t o_bytes = round256(rows * head_dim * sizeof(float));
     const size_t need = o_bytes + round256(rows * sizeof(float));
-    if (!workspace || ws_bytes < need)
+    if (noalloc && need > fa::kDecodeScratchBytes)
+        return fail(FA_ERR_WORKSPACE,
+                    "%s: the split partials need %zu bytes, above the %zu bytes of static "
+                    "scratch (batch x query heads x splits too large)",
+                    fn, need, fa::kDecodeScratchBytes);
+    if (!noalloc && (!workspace || ws_bytes < need))
         return fail(FA_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn,
                     workspace ? ws_bytes : (size_t)0, need);
     a.q = q;
@@ -492,6 +497,8 @@ fa_status decode_impl(const char *fn, bool ring, const void *q, void *o, float *
     a.n_layers = ring ? 1 : n_layers;
     a.layer = ring ? 0 : layer;
     a.sm_scale = sm_scale;
+    if (noalloc)
+        return hip_status(fa::launch_decode_noalloc(a, o_bytes, (hipStream_t)stream), fn);
     a.o_part = (float *)workspace;
     a.lse_part = (float *)((char *)workspace + o_bytes);
     return hip_status(fa::launch_decode(a, (hipStream_t)stream), fn);
@@ -510,10 +517,25 @@ fa_status fa_attn_decode(const void *q, void *o, float *lse, const void *k_new, 
                          int32_t block_tokens, float sm_scale, void *workspace, size_t ws_bytes,
                          void *stream)
 {
-    return decode_impl("fa_attn_decode", false, q, o, lse, k_new, v_new, k_cache, v_cache,
-                       max_cache, cache_len, dtype, batch, n_q_heads, n_kv_heads, head_dim, route,
-                       route_host, n_layers, layer, sink_tokens, window_tokens, block_tokens,
-                       sm_scale, workspace, ws_bytes, stream);
+    return decode_impl("fa_attn_decode", false, false, q, o, lse, k_new, v_new, k_cache,
+                       v_cache, max_cache, cache_len, dtype, batch, n_q_heads, n_kv_heads,
+                       head_dim, route, route_host, n_layers, layer, sink_tokens, window_tokens,
+                       block_tokens, sm_scale, workspace, ws_bytes, stream);
+}
+
+fa_status fa_attn_decode_noalloc(const void *q, void *o, float *lse, const void *k_new,
+                                 const void *v_new, void *k_cache, void *v_cache,
+                                 int32_t max_cache, const int32_t *cache_len, int32_t dtype,
+                                 int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                 int32_t head_dim, const uint8_t *route,
+                                 const uint8_t *route_host, int32_t n_layers, int32_t layer,
+                                 int32_t sink_tokens, int32_t window_tokens,
+                                 int32_t block_tokens, float sm_scale, void *stream)
+{
+    return decode_impl("fa_attn_decode_noalloc", false, true, q, o, lse, k_new, v_new, k_cache,
+                       v_cache, max_cache, cache_len, dtype, batch, n_q_heads, n_kv_heads,
+                       head_dim, route, route_host, n_layers, layer, sink_tokens, window_tokens,
+                       block_tokens, sm_scale, nullptr, 0, stream);
 }
 
 fa_status fa_attn_decode_ring(const void *q, void *o, float *lse, const void *k_new,
@@ -523,7 +545,7 @@ fa_status fa_attn_decode_ring(const void *q, void *o, float *lse, const void *k_
                               int32_t sink_tokens, int32_t window_tokens, int32_t block_tokens,
                               float sm_scale, void *workspace, size_t ws_bytes, void *stream)
 {
-    return decode_impl("fa_attn_decode_ring", true, q, o, lse, k_new, v_new, k_ring, v_ring,
+    return decode_impl("fa_attn_decode_ring", true, false, q, o, lse, k_new, v_new, k_ring, v_ring,
                        ring_tokens, cache_len, dtype, batch, n_q_heads, n_kv_heads, head_dim,
                        nullptr, nullptr, 1, 0, sink_tokens, window_tokens, block_tokens, sm_scale,
                        workspace, ws_bytes, stream);

@@ -16,6 +16,8 @@
 // the row slots and then the 4 wavefronts are merged with the log-sum-exp rule
 // through LDS.  A second small kernel merges the splits in ascending order.
 // Both merges use fixed orders, so results are bitwise reproducible.
+#include <mutex>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -691,6 +693,58 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
             a.o_part, a.lse_part, a.cache_len, max_len, a.hq, a.d, a.n_splits, (float *)a.o,
             a.lse);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the no-allocation decode entry point: the split partials live in
+// this file-scope device array (one copy per GPU the library runs on, held until
+// the process ends) instead of a caller workspace.  Host code never uses the
+// array's name as an address: on first use on a device its device address is
+// looked up once with that device current and kept per device.  Nothing in it
+// has to start at zero (every split writes its partial before the merge reads
+// it); calls that overlap on one GPU share it and race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char fa_decode_scratch[kDecodeScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices] = {};
+
+hipError_t decode_scratch_ptr(hipStream_t stream, void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess) return e;
+        if (sdev != dev) return hipErrorInvalidDevice;  // the stream's device must be current
+    }
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(fa_decode_scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_decode_noalloc(DecodeArgs a, size_t o_bytes, hipStream_t stream)
+{
+    void *base = nullptr;
+    hipError_t e = decode_scratch_ptr(stream, &base);
+    if (e != hipSuccess) return e;
+    a.o_part = (float *)base;
+    a.lse_part = (float *)((char *)base + o_bytes);
+    return launch_decode(a, stream);
 }
 
 namespace {

@@ -85,6 +85,11 @@ struct DecodeArgs {
     float *lse_part;   // [batch][hq][n_splits]
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// The same launch with o_part / lse_part taken from the library's per-device
+// static scratch (kDecodeScratchBytes, held until the process ends) instead of
+// a caller workspace; the caller has checked that the partials fit.
+constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+hipError_t launch_decode_noalloc(DecodeArgs a, size_t o_bytes, hipStream_t stream);
 
 struct CompactArgs {
     const void *k, *v;

@@ -133,6 +133,14 @@ int main()
     EXPECT(fa_attn_decode(P, P, nullptr, nullptr, nullptr, P, P, 5000, CU, FA_BF16, 2, 96, 8,
                           128, RT, nullptr, 1, 0, 128, 2048, 64, sc, ws.data(), dws, nullptr),
            FA_ERR_UNSUPPORTED);
+    EXPECT(fa_attn_decode_noalloc(P, P, nullptr, P, P, P, P, 5000, CU, FA_BF16, 2, 32, 8, 128,
+                                  RT, r_mix, 1, 0, 128, 2048, 64, sc, nullptr), FA_OK);
+    EXPECT(fa_attn_decode_noalloc(P, P, nullptr, nullptr, nullptr, P, P, 1 << 20, CU, FA_BF16,
+                                  512, 32, 8, 128, RT, nullptr, 1, 0, 128, 2048, 64, sc, nullptr),
+           FA_ERR_WORKSPACE);
+    EXPECT(fa_attn_decode_noalloc(P, P, nullptr, P, nullptr, P, P, 5000, CU, FA_BF16, 2, 32, 8,
+                                  128, RT, nullptr, 1, 0, 128, 2048, 64, sc, nullptr),
+           FA_ERR_INVALID_ARG);
     const size_t rws2 = fa_decode_workspace_size(2, 32, 128, 2176);
     EXPECT(fa_attn_decode_ring(P, P, nullptr, P, P, P, P, 2176, CU, FA_BF16, 2, 32, 8, 128, 128,
                                2048, 64, sc, ws.data(), rws2, nullptr), FA_OK);

@@ -15,6 +15,7 @@ hipError_t launch_router(const RouterArgs &, hipStream_t) { ++g_launches; return
 hipError_t launch_block_plan(const PlanArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_prefill(const PrefillArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_decode(const DecodeArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_decode_noalloc(DecodeArgs, size_t, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_kv_compact(const CompactArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_xa_scores(const XaScoreArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_xa_select(const XaSelectArgs &, hipStream_t) { ++g_launches; return hipSuccess; }

@@ -27,14 +27,14 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     assert set(names) == set(_lib.EXPORTS)
     for name in names:
         assert hasattr(L, name), name
 
 
 def test_abi_version_and_clean_error_state():
-    assert _lib.fa_abi_version() == 7
+    assert _lib.fa_abi_version() == 8
 
 
 def test_workspace_sizes():
@@ -150,6 +150,23 @@ def decode_args(**kw):
 def test_decode_validation(kw, status):
     assert _lib.lib().fa_attn_decode(*decode_args(**kw)) == status
     assert _lib.last_error().startswith("fa_attn_decode")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kc=None), _lib.FA_ERR_INVALID_ARG),
+    (dict(k_new=P), _lib.FA_ERR_INVALID_ARG),   # v_new missing
+    (dict(layer=32), _lib.FA_ERR_INVALID_ARG),
+    (dict(d=80), _lib.FA_ERR_UNSUPPORTED),
+    # partials above the 64 MiB static scratch: 512 x 32 heads x 64 splits x 129 x 4 B
+    (dict(batch=512, max_cache=1 << 20), _lib.FA_ERR_WORKSPACE),
+])
+def test_decode_noalloc_validation(kw, status):
+    """The no-allocation variant validates like fa_attn_decode and refuses split
+    partials larger than its static scratch, before touching the GPU."""
+    a = decode_args(**kw)
+    del a[22:24]  # no workspace, no ws_bytes
+    assert _lib.lib().fa_attn_decode_noalloc(*a) == status
+    assert _lib.last_error().startswith("fa_attn_decode_noalloc")
 
 
 def test_decode_workspace_matches_sizing_function():
