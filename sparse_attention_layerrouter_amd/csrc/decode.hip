@@ -302,8 +302,12 @@ struct DecChunkRegs {
     u32x4 k[2][D / 32];   // [half][d step] K operand
 };
 
-template <int D, int G, int MODE, bool RING>
-__global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
+// ONE: every wave takes at most one chunk (splits of kWaves * kDecChunk tokens,
+// e.g. every split of an SA layer's sink + window span): no second register set
+// or V buffer, so four workgroups fit per CU and a short layer's splits run in
+// about one round.  The per-chunk arithmetic and the merges are the same.
+template <int D, int G, int MODE, bool RING, bool ONE>
+__global__ __launch_bounds__(kThreads, ONE ? 5 : 2) void decode_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_new,
     const uint16_t *__restrict__ v_new, uint16_t *__restrict__ k_cache,
     uint16_t *__restrict__ v_cache, int max_cache, const int32_t *__restrict__ cache_len,
@@ -319,10 +323,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
     static_assert(G >= 1 && G <= 16, "GQA ratio");
     // V buffers: [wave] x 2, two separate arrays so that reads of the current
     // chunk provably do not alias the copies into the next one
+    // ONE with G <= 8 keeps its whole LDS within the 32 KiB V buffer (the merge
+    // scratch then lives in it too), so five workgroups fit per CU
+    constexpr bool kPack = ONE && G <= 8;
+    constexpr int HS = kPack ? G : 16;  // head slots of the merge scratch
+    static_assert(kWaves * HS * D * 4 + (kPack ? 2 * kWaves * 16 * 4 : 0) <= kWaves * VBYTES,
+                  "merge scratch fits the V buffers");
     __shared__ __attribute__((aligned(1024))) char vbuf0[kWaves][VBYTES];
-    __shared__ __attribute__((aligned(1024))) char vbuf1[kWaves][VBYTES];
-    __shared__ float sm_m[kWaves][16];
-    __shared__ float sm_l[kWaves][16];
+    // (the unused arrays of a variant are never referenced and take no LDS)
+    __shared__ __attribute__((aligned(1024))) char vbuf1[ONE ? 1 : kWaves][ONE ? 16 : VBYTES];
+    __shared__ float sm_m_s[kPack ? 1 : kWaves * 16];
+    __shared__ float sm_l_s[kPack ? 1 : kWaves * 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -466,6 +477,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
         }
     };
 
+    if constexpr (ONE) {
+        const int cv = v0 + wave * kDecChunk;
+        if (cv < v1) {
+            DecChunkRegs<D> ra;
+            issue(cv, ra, vbuf0[wave]);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            compute(cv, ra, vbuf0[wave]);
+        }
+    } else {
     // software-pipelined chunk loop, unrolled by two so each step uses fixed buffers
     DecChunkRegs<D> ra, rb;
     const int stride = kWaves * kDecChunk;
@@ -485,21 +505,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
         compute(cn, rb, vbuf1[wave]);
         cv = cm;
     }
+    }
 
     // per-head totals of this wavefront: lanes l16 + 16*g4 share head l16
     float l_w = l_run + xor16(l_run);
     l_w = sum_xor32(l_w);
     // O^T: lane holds the finished sums for d = dt*16 + 4*g4 + j of head l16
     __syncthreads();  // every wave is done with its V buffers: reuse them for the merge
-    float *sm_o = (float *)&vbuf0[0][0];   // [wave][16][D] floats (32 KiB at D = 128)
+    float *sm_o = (float *)&vbuf0[0][0];   // [wave][HS][D] floats (<= 32 KiB at D = 128)
+    float *sm_m = kPack ? sm_o + kWaves * HS * D : sm_m_s;  // [wave][16]
+    float *sm_l = kPack ? sm_m + kWaves * 16 : sm_l_s;      // [wave][16]
+    if (l16 < HS) {
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
+        for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            sm_o[((size_t)wave * 16 + l16) * D + dt * 16 + 4 * g4 + j] = oacc[dt][j];
+            for (int j = 0; j < 4; ++j)
+                sm_o[((size_t)wave * HS + l16) * D + dt * 16 + 4 * g4 + j] = oacc[dt][j];
+    }
     if (g4 == 0) {
-        sm_m[wave][l16] = m_run;
-        sm_l[wave][l16] = l_w;
+        sm_m[wave * 16 + l16] = m_run;
+        sm_l[wave * 16 + l16] = l_w;
     }
     __syncthreads();
 
@@ -508,14 +533,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
         const int h = idx / D, d = idx % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 16 + h]);
         const float Mu = M == -INFINITY ? 0.0f : M;
         float L = 0.0f, O = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float f = fast_exp2(sm_m[w][h] - Mu);
-            L += sm_l[w][h] * f;
-            O += sm_o[((size_t)w * 16 + h) * D + d] * f;
+            const float f = fast_exp2(sm_m[w * 16 + h] - Mu);
+            L += sm_l[w * 16 + h] * f;
+            O += sm_o[((size_t)w * HS + h) * D + d] * f;
         }
         const size_t row = ((size_t)b * hq + kvh * G + h) * n_splits + split;
         o_part[row * D + d] = L > 0.0f ? O / L : 0.0f;
@@ -627,14 +652,24 @@ hipError_t launch_bf16(const DecodeArgs &a, hipStream_t stream, const SparseRule
         (uint16_t *)a.k_cache, (uint16_t *)a.v_cache, a.max_cache, a.cache_len, a.route,          \
         a.n_layers, a.layer, a.hq, a.hkv, r, scale_log2, a.split_tokens, a.n_splits, a.o_part,    \
         a.lse_part
-    if (a.ring)
-        decode_bf16_kernel<D, G, kModeSA, true><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
-    else if (a.mode == kModeFA)
-        decode_bf16_kernel<D, G, kModeFA, false><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
-    else if (a.mode == kModeSA)
-        decode_bf16_kernel<D, G, kModeSA, false><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
-    else
-        decode_bf16_kernel<D, G, kModeMixed, false><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
+    if (a.split_tokens == kWaves * kDecChunk) {  // one chunk per wave
+        if (a.ring)
+            decode_bf16_kernel<D, G, kModeSA, true, true><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
+        else if (a.mode == kModeFA)
+            decode_bf16_kernel<D, G, kModeFA, false, true><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
+        else if (a.mode == kModeSA)
+            decode_bf16_kernel<D, G, kModeSA, false, true><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
+        else
+            decode_bf16_kernel<D, G, kModeMixed, false, true><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
+    } else if (a.ring) {
+        decode_bf16_kernel<D, G, kModeSA, true, false><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
+    } else if (a.mode == kModeFA) {
+        decode_bf16_kernel<D, G, kModeFA, false, false><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
+    } else if (a.mode == kModeSA) {
+        decode_bf16_kernel<D, G, kModeSA, false, false><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
+    } else {
+        decode_bf16_kernel<D, G, kModeMixed, false, false><<<grid, kThreads, 0, stream>>>(FA_DEC16_ARGS);
+    }
 #undef FA_DEC16_ARGS
     return hipGetLastError();
 }
