@@ -8,13 +8,14 @@
         HBM bytes per launch of the hot kernels from FETCH_SIZE / WRITE_SIZE
         passes (KiB per dispatch), each scaled by what the same counter reads
         for a plain 1 GiB read + 1 GiB write elementwise kernel.
-    python -m sparse_attention_layerrouter_amd.rocprof_summary mfma DIR PROFILE_JSON OUT_JSON
-        matrix-core evidence of the hot kernels from one counter pass with
-        SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE
-        and SQ_BUSY_CU_CYCLES (plus --kernel-trace for durations): executed MFMA
-        flops (MOPS x 512) against the algorithmic flops bench.py --profile
-        printed (PROFILE_JSON), the share of SIMD cycles the matrix cores were
-        busy, and the clock the kernel ran at.
+    python -m sparse_attention_layerrouter_amd.rocprof_summary counters DIR [DIR ...] \\
+            PROFILE_JSON OUT_JSON
+        per hot kernel, the mean of every counter of one or more counter passes
+        (each run with --kernel-trace for durations) over its dispatches, and what
+        follows from them: executed MFMA flops (MOPS x 512) against the
+        algorithmic flops bench.py --profile printed (PROFILE_JSON), the clock,
+        the matrix-core, LDS and VALU busy shares, LDS read bytes per clock,
+        bank conflicts and the share of wave cycles spent waiting.
 """
 from __future__ import annotations
 
@@ -31,8 +32,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 HOT_KERNELS = {
     "prefill_bf16_fa_131k": ("prefill_bf16_kernel<128, 1>", ("prefill.hip", "fa_common.h")),
     "prefill_bf16_sa_131k": ("prefill_bf16_kernel<128, 2>", ("prefill.hip", "fa_common.h")),
-    "decode_bf16_fa_131k": ("decode_bf16_kernel<128, 4, 1, false>", ("decode.hip", "fa_common.h")),
-    "decode_bf16_sa_131k": ("decode_bf16_kernel<128, 4, 2, false>", ("decode.hip", "fa_common.h")),
+    "decode_bf16_fa_131k": ("decode_bf16_kernel<128, 4, 1, false, false>", ("decode.hip", "fa_common.h")),
+    "decode_bf16_sa_131k": ("decode_bf16_kernel<128, 4, 2, false, true>", ("decode.hip", "fa_common.h")),
 }
 COPY_BYTES = 1 << 30
 
@@ -105,12 +106,11 @@ def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_json):
     return out
 
 
-# SIMDs of an MI355X (256 CUs x 4) and XCDs; GRBM_GUI_ACTIVE is reported summed over
-# the 8 XCDs, each of which counts the same active cycles
+# SIMDs and CUs of an MI355X (256 CUs x 4 SIMDs) and XCDs; GRBM_GUI_ACTIVE is
+# reported summed over the 8 XCDs, each of which counts the same active cycles
 N_SIMD = 1024
+N_CU = 256
 N_XCD = 8
-MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE",
-                 "SQ_BUSY_CU_CYCLES")
 
 
 def _durations(directory):
@@ -124,47 +124,70 @@ def _durations(directory):
     return out
 
 
-def mfma(directory, profile_json, out_json):
+def counters(directories, profile_json, out_json):
+    """Per hot kernel: the mean of every counter over its dispatches (the passes in
+    `directories` may collect different counters of the same program), and the
+    figures derived from those present."""
     with open(profile_json) as f:
         prof = json.load(f)
     alg = prof.get("algorithmic", {})
-    dur = _durations(directory)
-    per = {}  # kernel key -> dispatch -> {counter: value}
-    for r in _rows(directory, "counter_collection.csv"):
-        cname = r.get("Counter_Name")
-        if cname not in MFMA_COUNTERS:
-            continue
-        for key, (needle, _) in HOT_KERNELS.items():
-            if needle in r["Kernel_Name"]:
-                d = per.setdefault(key, {}).setdefault(r["Dispatch_Id"], {})
-                d[cname] = d.get(cname, 0.0) + float(r["Counter_Value"])
-    out = {"_note": ("per kernel: mean over its dispatches. executed_flop = MOPS_BF16 x 512; "
-                     "mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 "
-                     "SIMDs), the MfmaUtil expression; clock = GRBM_GUI_ACTIVE / 8 / kernel "
-                     "duration; cu_busy = SQ_BUSY_CU_CYCLES x 4 / (GRBM_GUI_ACTIVE / 8 x 256)"),
+    out = {"_note": ("mean over each kernel's dispatches of every counter, per pass; derived: "
+                     "executed_flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; cycles = "
+                     "GRBM_GUI_ACTIVE / 8 (per-XCD active cycles); clock = cycles / "
+                     "duration; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs) "
+                     "(the MfmaUtil expression); lds_util = SQ_LDS_IDX_ACTIVE / (cycles x 256 "
+                     "CUs) (LdsUtil); lds_read_bytes_per_clk_per_cu = "
+                     "SQ_INSTS_LDS_LOAD_BANDWIDTH x 64 / (cycles x 256); valu_busy = "
+                     "SQ_ACTIVE_INST_VALU / (cycles x 256) (VALUBusy); wait_fraction = "
+                     "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES"),
            "_workload": {k: v for k, v in prof.items() if k != "algorithmic"}}
-    for key, dispatches in per.items():
-        n = len(dispatches)
-        mean = {c: sum(d.get(c, 0.0) for d in dispatches.values()) / n for c in MFMA_COUNTERS}
-        durs = [dur[i] for i in dispatches if i in dur]
-        dns = sum(durs) / len(durs) if durs else None
-        gui = mean["GRBM_GUI_ACTIVE"] / N_XCD
-        e = {"kernel": HOT_KERNELS[key][0], "dispatches": n, "counters_mean": mean,
-             "duration_us": dns / 1e3 if dns else None,
-             "executed_flop": mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0,
-             "mfma_busy": mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * N_SIMD) if gui else None,
-             "cu_busy": mean["SQ_BUSY_CU_CYCLES"] * 4.0 / (gui * 256) if gui else None,
-             "clock_ghz": gui / dns if dns else None}
-        a = alg.get(key, {}).get("flop")
-        if a:
-            e["algorithmic_flop"] = a
-            e["executed_over_algorithmic"] = e["executed_flop"] / a
-            if dns:
-                e["algorithmic_tflops"] = a / dns / 1e3
-                # the same rate against the peak at the clock the kernel ran at
-                e["peak_at_clock_tflops"] = 256 * 4096 * e["clock_ghz"] * 1e9 / 1e12
-        e["source_hash"] = source_hash(*HOT_KERNELS[key][1])
-        out[key] = e
+    for directory in directories:
+        dur = _durations(directory)
+        per = {}  # kernel key -> dispatch -> {counter: value}
+        for r in _rows(directory, "counter_collection.csv"):
+            for key, (needle, _) in HOT_KERNELS.items():
+                if needle in r["Kernel_Name"]:
+                    d = per.setdefault(key, {}).setdefault(r["Dispatch_Id"], {})
+                    c = r["Counter_Name"]
+                    d[c] = d.get(c, 0.0) + float(r["Counter_Value"])
+        for key, dispatches in per.items():
+            e = out.setdefault(key, {"kernel": HOT_KERNELS[key][0],
+                                     "source_hash": source_hash(*HOT_KERNELS[key][1]),
+                                     "passes": []})
+            names = sorted({c for d in dispatches.values() for c in d})
+            mean = {c: sum(d.get(c, 0.0) for d in dispatches.values()) / len(dispatches)
+                    for c in names}
+            durs = [dur[i] for i in dispatches if i in dur]
+            dns = sum(durs) / len(durs) if durs else None
+            p = {"dispatches": len(dispatches), "counters_mean": mean,
+                 "duration_us": dns / 1e3 if dns else None}
+            cyc = mean.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+            if cyc and dns:
+                p["clock_ghz"] = cyc / dns
+            if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in mean:
+                p["executed_flop"] = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
+                a = alg.get(key, {}).get("flop")
+                if a:
+                    p["algorithmic_flop"] = a
+                    p["executed_over_algorithmic"] = p["executed_flop"] / a
+                    if dns:
+                        p["algorithmic_tflops"] = a / dns / 1e3
+            if cyc:
+                for name, num, den in (
+                        ("mfma_busy", "SQ_VALU_MFMA_BUSY_CYCLES", cyc * N_SIMD),
+                        ("lds_util", "SQ_LDS_IDX_ACTIVE", cyc * N_CU),
+                        ("valu_busy", "SQ_ACTIVE_INST_VALU", cyc * N_CU)):
+                    if num in mean:
+                        p[name] = mean[num] / den
+                if "SQ_INSTS_LDS_LOAD_BANDWIDTH" in mean:
+                    p["lds_read_bytes_per_clk_per_cu"] = (
+                        mean["SQ_INSTS_LDS_LOAD_BANDWIDTH"] * 64.0 / (cyc * N_CU))
+            if "SQ_WAIT_INST_ANY" in mean and mean.get("SQ_WAVE_CYCLES"):
+                p["wait_fraction"] = mean["SQ_WAIT_INST_ANY"] / mean["SQ_WAVE_CYCLES"]
+            if "SQ_LDS_BANK_CONFLICT" in mean and mean.get("SQ_LDS_IDX_ACTIVE"):
+                p["lds_bank_conflict_per_active"] = (mean["SQ_LDS_BANK_CONFLICT"] /
+                                                     mean["SQ_LDS_IDX_ACTIVE"])
+            e["passes"].append(p)
     with open(out_json, "w") as f:
         json.dump(out, f, indent=1)
     return out
@@ -175,8 +198,8 @@ if __name__ == "__main__":
         print(stats(sys.argv[2]))
     elif len(sys.argv) == 7 and sys.argv[1] == "traffic":
         print(json.dumps(traffic(*sys.argv[2:7]), indent=1))
-    elif len(sys.argv) == 5 and sys.argv[1] == "mfma":
-        print(json.dumps(mfma(*sys.argv[2:5]), indent=1))
+    elif len(sys.argv) >= 5 and sys.argv[1] == "counters":
+        print(json.dumps(counters(sys.argv[2:-2], sys.argv[-2], sys.argv[-1]), indent=1))
     else:
         print(__doc__)
         sys.exit(2)
