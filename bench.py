@@ -183,6 +183,62 @@ def cpu_info():
     return model, cores
 
 
+class ClockSampler:
+    """Samples the graphics clocks with `amd-smi metric --clock --json` from a
+    background thread while a timed region runs (best effort: no samples when the
+    tool is missing or its output cannot be read).  The value per sample is the
+    mean current clock over the device's graphics domains (one per XCD)."""
+
+    def __init__(self):
+        import shutil
+        import threading
+
+        self.exe = shutil.which("amd-smi") or (
+            "/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._poll, daemon=True)
+
+    def _read(self):
+        import subprocess
+
+        r = subprocess.run([self.exe, "metric", "--clock", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        d = json.loads(r.stdout)
+        if isinstance(d, dict):
+            d = d.get("gpu_data", [d])
+        clk = d[0]["clock"]
+        vals = [v["clk"]["value"] for k, v in clk.items()
+                if k.startswith("gfx") and isinstance(v, dict) and isinstance(v.get("clk"), dict)
+                and isinstance(v["clk"].get("value"), (int, float))]
+        return sum(vals) / len(vals) if vals else None
+
+    def _poll(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v is not None:
+                    self.samples.append(v)
+            except Exception:  # best effort: a failed read is just no sample
+                pass
+            self._stop.wait(0.25)
+
+    def start(self):
+        if self.exe:
+            self._thread.start()
+        return self
+
+    def stop(self, during: str):
+        if self.exe:
+            self._stop.set()
+            self._thread.join(timeout=30)
+        if not self.samples:
+            return None
+        out = dist(self.samples)
+        return {"unit": "MHz", "during": during, "source": "amd-smi metric --clock",
+                **{k: (round(v, 1) if isinstance(v, float) else v) for k, v in out.items()}}
+
+
 # ---------------------------------------------------------------------------
 
 def main():
@@ -323,11 +379,13 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
     recs = []
+    clocks = ClockSampler().start()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(recs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gpu_clock = clocks.stop("the timed steps (about 95 % of their time is FA prefill layers)")
     log(f"timed {args.steps} steps in {wall:.2f} s")
 
     route_full = route.clone()  # the sweeps below re-run the router on shorter inputs
@@ -766,6 +824,7 @@ def main():
             "serving_sweep_32k": serving,
         },
         "timing": timing,
+        "gpu_clock_mhz": gpu_clock,
         "roofline": {
             "kernel": "prefill_bf16_kernel<128> (FA layer, 131072 tokens)",
             "bound": "mfma", "achieved": round(achieved_tflops, 1),
@@ -1184,9 +1243,9 @@ def cpu_baseline(args, qkv, route_np, T, scale, t_prefill_gpu):
 def cpu_full(stream):
     """Unsampled oracle runs, timed on every core the process may use, with full-row
     parity of the same GPU launches: the tiny two-layer case (router + FA + SA, fp32),
-    one SA layer at 32768 tokens (Llama shape, bf16; an FA layer at that size is
-    sampled and extrapolated), and one FA and one SA decode layer at batch 8 over
-    131072-token caches (every head)."""
+    one SA and one FA layer at 32768 tokens (Llama shape, bf16; the FA layer runs in
+    eight row chunks, each logged, as it takes minutes), and one FA and one SA decode
+    layer at batch 8 over 131072-token caches (every head)."""
     import numpy as np
     import torch
 
@@ -1232,7 +1291,7 @@ def cpu_full(stream):
         "tolerance": 1e-4}
     log("cpu-full: tiny case done")
 
-    # ---- one SA layer at 32768 tokens (every row), one FA layer sampled
+    # ---- one SA and one FA layer at 32768 tokens, every row
     T2 = 32768
     q = synth.device_normal((T2, HQ, D), seed=0)
     k = synth.device_normal((T2, HKV, D), seed=1)
@@ -1247,21 +1306,19 @@ def cpu_full(stream):
         gpu_ms = _time_calls(stream, lambda: _lib.fa_attn_prefill(
             q, k, v, o, cu2, T2, torch.from_numpy(r).to(dev), 0, SINK, WINDOW, BLOCK, sc,
             lse=lse, route_host=r), 2, 5)
-        rows = None if not bit else np.sort(
-            np.random.default_rng(3).choice(T2, 512, replace=False)).astype(np.int32)
-        t0 = time.perf_counter()
-        o_ref, l_ref = oracle.attn_prefill(qh, kh, vh, [0, T2], r, 0, SINK, WINDOW, BLOCK, sc,
-                                           rows=rows, n_threads=cores)
-        dt = time.perf_counter() - t0
-        sel = np.arange(T2) if rows is None else rows
-        e = _parity_entry(_f64(_host_bits(o)[sel]), o_ref, lse.cpu().numpy()[sel], l_ref)
-        pairs = pairs_sa(T2) if not bit else pairs_fa(T2)
-        done = _sa_row_pairs(sel) if not bit else int((sel + 1).sum())
-        out[name] = {"kind": "full" if rows is None else "extrapolated",
-                     "rows": int(sel.size), "seconds": round(dt, 3),
-                     "seconds_full_layer": round(dt * pairs / done, 2),
+        parts, dt = [], 0.0
+        for rows in np.array_split(np.arange(T2, dtype=np.int32), 8 if bit else 1):
+            t0 = time.perf_counter()
+            parts.append(oracle.attn_prefill(qh, kh, vh, [0, T2], r, 0, SINK, WINDOW, BLOCK,
+                                             sc, rows=rows, n_threads=cores))
+            dt += time.perf_counter() - t0
+            log(f"cpu-full: {name} rows {rows[0]}..{rows[-1]} ({dt:.0f} s so far)")
+        o_ref = np.concatenate([p_[0] for p_ in parts])
+        l_ref = np.concatenate([p_[1] for p_ in parts])
+        e = _parity_entry(_f64(_host_bits(o)), o_ref, lse.cpu().numpy(), l_ref)
+        out[name] = {"kind": "full", "rows": T2, "seconds": round(dt, 3),
                      "gpu_ms": dist(gpu_ms),
-                     "cpu_over_gpu": round(dt * pairs / done / (np.median(gpu_ms) * 1e-3), 1),
+                     "cpu_over_gpu": round(dt / (np.median(gpu_ms) * 1e-3), 1),
                      "parity": e}
         log(f"cpu-full: {name} {dt:.1f} s")
     del q, k, v, o
