@@ -409,6 +409,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
     float m_run = -INFINITY;  // reference max, log2 domain
+    float m_ref = 0.0f;       // the reference the scores are shifted by (0 while m_run = -inf)
+    float p_lim = -1.0f;      // fast-path bound on a lane's sum (-1: no reference yet)
     float l_run = 0.0f;       // this lane's share of the row sum
     f32x16 s[2];              // S^T of the current tile (two 32-key blocks)
     uint32_t pk[2][8];        // P of the previous tile, bf16 pairs (0: none)
@@ -539,7 +541,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         // a row, or scores that grew by many octaves) the tile max moves the
         // reference, O and l are rescaled and p is recomputed.  O / l does not
         // depend on the reference, so the result is the same softmax.
-        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+        const float m_use = m_ref;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -560,7 +562,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
             return q1[0];
         };
         float psum = row_sum();
-        const bool fast = m_run != -INFINITY && psum <= kFastLimit;  // NaN: not fast
+        const bool fast = psum <= p_lim;  // NaN, or no reference yet: not fast
         if (__builtin_amdgcn_ballot_w64(!fast) != 0) {
             float m1[11];
 #pragma unroll
@@ -580,7 +582,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
             m_run = m_new;
-            const float shift = m_use - (m_run == -INFINITY ? 0.0f : m_run);
+            m_ref = m_run == -INFINITY ? 0.0f : m_run;
+            p_lim = m_run == -INFINITY ? -1.0f : kFastLimit;
+            const float shift = m_use - m_ref;
 #pragma unroll
             for (int i = 0; i < 32; ++i) e[i] = fast_exp2(s[i >> 4][i & 15] + shift);
             psum = row_sum();
