@@ -73,11 +73,6 @@ int route_mode(const uint8_t *route_host, int batch, int n_layers, int layer)
     return fa::kModeMixed;
 }
 
-size_t decode_splits_cap(int max_cache)
-{
-    int s = fa::decode_n_splits(max_cache);
-    return (size_t)(s > 64 ? s : 64);
-}
 
 // Shared by fa_attn_prefill (queries = keys), fa_attn_prefill_kv and
 // fa_attn_prefill_triangle (tail_tokens > 0: the last tail_tokens rows of each
@@ -412,7 +407,7 @@ size_t fa_decode_workspace_size(int32_t batch, int32_t n_q_heads, int32_t head_d
                                 int32_t max_cache)
 {
     if (batch <= 0 || n_q_heads <= 0 || head_dim <= 0 || max_cache <= 0) return 0;
-    const size_t rows = (size_t)batch * n_q_heads * decode_splits_cap(max_cache);
+    const size_t rows = (size_t)batch * n_q_heads * fa::decode_max_splits(max_cache);
     return round256(rows * head_dim * sizeof(float)) + round256(rows * sizeof(float));
 }
 
@@ -466,8 +461,8 @@ fa_status decode_impl(const char *fn, bool ring, bool noalloc, const void *q, vo
     int max_kept = max_cache;
     if (a.mode == fa::kModeSA && sink_tokens + window_tokens < max_kept)
         max_kept = sink_tokens + window_tokens;
-    a.split_tokens = fa::decode_split_tokens(max_kept);
-    a.n_splits = fa::decode_n_splits(max_kept);
+    a.split_tokens = fa::decode_split_tokens(max_kept, batch * n_q_heads);
+    a.n_splits = fa::decode_n_splits(max_kept, batch * n_q_heads);
     const size_t rows = (size_t)batch * n_q_heads * a.n_splits;
     const size_t o_bytes = round256(rows * head_dim * sizeof(float));
     const size_t need = o_bytes + round256(rows * sizeof(float));

@@ -139,20 +139,42 @@ struct XaSelectArgs {
 };
 hipError_t launch_xa_select(const XaSelectArgs &a, hipStream_t stream);
 
-// Split policy shared by fa_decode_workspace_size and fa_attn_decode: about 64
-// splits per (sequence, kv head), 128..4096 tokens per split, a multiple of 64.
-inline int decode_split_tokens(int max_kept_tokens)
+// Split policy shared by fa_decode_workspace_size and fa_attn_decode; rows =
+// batch x query heads.  About 64 splits per (sequence, kv head), or fewer when
+// rows is large: min(64, kDecodeSplitRows / rows) above kDecodeShortKept kept
+// tokens, so a long-cache layer launches about 2048 workgroups at G = 4 (a few
+// rounds at two per CU) rather than up to 16384 short ones, whose partials and
+// merge cost more than the finer split balances.  Ranges up to kDecodeShortKept
+// tokens (every SA layer) keep about 64.  128..4096 tokens per split, a
+// multiple of 64.
+constexpr int kDecodeShortKept = 8192;
+constexpr int kDecodeSplitRows = 8192;
+inline int decode_split_target(int max_kept_tokens, int rows)
 {
-    int st = (max_kept_tokens + 63) / 64;
+    if (max_kept_tokens <= kDecodeShortKept) return 64;
+    const int t = kDecodeSplitRows / (rows > 0 ? rows : 1);
+    return t < 1 ? 1 : (t > 64 ? 64 : t);
+}
+inline int decode_split_tokens(int max_kept_tokens, int rows)
+{
+    const int target = decode_split_target(max_kept_tokens, rows);
+    int st = (max_kept_tokens + target - 1) / target;
     st = (st + 63) / 64 * 64;
     if (st < 128) st = 128;
     if (st > 4096) st = 4096;
     return st;
 }
-inline int decode_n_splits(int max_kept_tokens)
+inline int decode_n_splits(int max_kept_tokens, int rows)
 {
-    int st = decode_split_tokens(max_kept_tokens);
+    int st = decode_split_tokens(max_kept_tokens, rows);
     return (max_kept_tokens + st - 1) / st;
+}
+// The most splits a call with at most max_cache kept tokens can use: 64 (the
+// target never exceeds it), or max_cache / 4096 where the split size is capped.
+inline int decode_max_splits(int max_cache)
+{
+    const int c = (max_cache + 4095) / 4096;
+    return c > 64 ? c : 64;
 }
 
 }  // namespace fa

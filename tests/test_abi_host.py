@@ -44,9 +44,11 @@ def test_workspace_sizes():
     n = _lib.fa_decode_workspace_size(8, 32, 128, 131072)
     assert n == 8 * 32 * 64 * 128 * 4 + 8 * 32 * 64 * 4
     assert _lib.fa_decode_workspace_size(8, 32, 128, 0) == 0
-    # longer caches need more splits
+    # longer caches need more splits once the 4096-token split cap binds
     assert _lib.fa_decode_workspace_size(1, 1, 128, 1 << 20) > _lib.fa_decode_workspace_size(
         1, 1, 128, 1 << 17)
+    assert _lib.fa_decode_workspace_size(8, 32, 128, 1 << 20) == (
+        8 * 32 * 256 * 128 * 4 + 8 * 32 * 256 * 4)
 
 
 def prefill_args(**kw):
