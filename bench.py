@@ -253,7 +253,7 @@ def main():
     import torch
 
     from sparse_attention_layerrouter_amd import _lib, synth
-    from sparse_attention_layerrouter_amd.rocprof_summary import source_hash
+    from sparse_attention_layerrouter_amd.rocprof_summary import HOT_KERNELS, source_hash
 
     _lib.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
@@ -772,8 +772,8 @@ def main():
     fa_flop = flops_of_pairs(pairs_fa(T))
     sa_flop = flops_of_pairs(pairs_sa(T))
     achieved_tflops = fa_flop / t_fa / 1e12
-    pre_hash = source_hash("prefill.hip", "fa_common.h")
-    dec_hash = source_hash("decode.hip", "fa_common.h")
+    pre_hash = source_hash(*HOT_KERNELS["prefill_bf16_fa_131k"][1])
+    dec_hash = source_hash(*HOT_KERNELS["decode_bf16_fa_131k"][1])
     traffic_pre = read_traffic("prefill_bf16_fa_131k", pre_hash)
     dec_bytes = NB * HKV * NC * D * 2 * 2 + 2 * NB * HQ * D * 2
     dec_sa_bytes = NB * HKV * kept_tokens_decode(NC, False) * D * 2 * 2 + 2 * NB * HQ * D * 2

@@ -29,11 +29,14 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 # kernels whose traffic the benchmark reports, by a substring of the demangled name
+# (the launch header holds the decode split policy, which sets a decode launch's grid)
 HOT_KERNELS = {
     "prefill_bf16_fa_131k": ("prefill_bf16_kernel<128, 1>", ("prefill.hip", "fa_common.h")),
     "prefill_bf16_sa_131k": ("prefill_bf16_kernel<128, 2>", ("prefill.hip", "fa_common.h")),
-    "decode_bf16_fa_131k": ("decode_bf16_kernel<128, 4, 1, false, false>", ("decode.hip", "fa_common.h")),
-    "decode_bf16_sa_131k": ("decode_bf16_kernel<128, 4, 2, false, true>", ("decode.hip", "fa_common.h")),
+    "decode_bf16_fa_131k": ("decode_bf16_kernel<128, 4, 1, false, false>",
+                            ("decode.hip", "fa_common.h", "fa_launch.h")),
+    "decode_bf16_sa_131k": ("decode_bf16_kernel<128, 4, 2, false, true>",
+                            ("decode.hip", "fa_common.h", "fa_launch.h")),
 }
 COPY_BYTES = 1 << 30
 
