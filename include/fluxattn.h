@@ -394,7 +394,7 @@ fa_status fa_attn_decode(const void *q, void *o, float *lse, const void *k_new,
  * stream, or events).
  * Errors: as fa_attn_decode; partials larger than the array (batch x n_q_heads
  * x splits x (head_dim + 1) x 4 bytes above 64 MiB, e.g. batch 64 with 32 heads,
- * head_dim 128 and 64 splits of a long cache) -> FA_ERR_WORKSPACE; a stream of
+ * head_dim 128 and an 8192-token cache, 64 splits) -> FA_ERR_WORKSPACE; a stream of
  * another device -> FA_ERR_HIP.
  */
 fa_status fa_attn_decode_noalloc(const void *q, void *o, float *lse,

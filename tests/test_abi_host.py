@@ -159,7 +159,8 @@ def test_decode_validation(kw, status):
     (dict(k_new=P), _lib.FA_ERR_INVALID_ARG),   # v_new missing
     (dict(layer=32), _lib.FA_ERR_INVALID_ARG),
     (dict(d=80), _lib.FA_ERR_UNSUPPORTED),
-    # partials above the 64 MiB static scratch: 512 x 32 heads x 64 splits x 129 x 4 B
+    # partials above the 64 MiB static scratch: 512 x 32 heads x 256 splits of 4096
+    # tokens x 129 x 4 B
     (dict(batch=512, max_cache=1 << 20), _lib.FA_ERR_WORKSPACE),
 ])
 def test_decode_noalloc_validation(kw, status):

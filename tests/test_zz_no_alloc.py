@@ -57,8 +57,8 @@ def test_noalloc_decode_matches_workspace_decode(dtype):
 
 
 def test_noalloc_rejects_partials_above_the_scratch():
-    """Host-side size check: batch 512 with 32 heads and 64 splits needs more than the
-    64 MiB scratch; nothing is launched."""
+    """Host-side size check: batch 512 with 32 heads and 32 splits (a 4096-token
+    cache) needs more than the 64 MiB scratch; nothing is launched."""
     q = torch.empty((512, 32, 128), dtype=torch.bfloat16, device=DEV)
     kc = torch.empty((512, 8, 4096, 128), dtype=torch.bfloat16, device=DEV)
     cl = torch.full((512,), 4096, dtype=torch.int32, device=DEV)
