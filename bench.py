@@ -133,6 +133,16 @@ def kept_tokens_decode(n: int, is_fa: bool, sink=SINK, window=WINDOW, block=BLOC
     return sink_len + n - win_start
 
 
+def load_oracle():
+    """The CPU oracle (test infrastructure) for the CPU-baseline leg only: the oracle's
+    timing with its sampled parity (cpu_baseline), the needle-row parity, the Qwen
+    decode loop's last-step check and the unsampled runs of --cpu-full.  With
+    --no-cpu-baseline none of them runs and the oracle is never loaded."""
+    import oracle
+
+    return oracle
+
+
 def read_traffic(kernel_key: str, src_hash: str):
     """HBM traffic per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source; else None."""
@@ -962,7 +972,6 @@ def qwen_leg(args, stream):
     import numpy as np
     import torch
 
-    import oracle
     from sparse_attention_layerrouter_amd import _lib, synth
 
     dev = torch.device("cuda:0")
@@ -1069,8 +1078,10 @@ def qwen_leg(args, stream):
     allfa_ms = decode_loop(allfa_np, NS)
     log("qwen decode loops timed")
 
-    # ---- the last routed step against the oracle on the grown caches: a layer with
-    # mixed routes, an all-FA and an all-SA layer (when the mask has them), KV heads 0, 7
+    # ---- (CPU-baseline leg) the last routed step against the oracle on the grown
+    # caches: a layer with mixed routes, an all-FA and an all-SA layer (when the mask
+    # has them), KV heads 0, 7
+    oracle = None if args.no_cpu_baseline else load_oracle()
     G = HQ // HKV
     n_fa = qr_np.sum(axis=0)
     picks = {}
@@ -1078,9 +1089,9 @@ def qwen_leg(args, stream):
         idx = np.nonzero(sel)[0]
         if idx.size:
             picks[kind] = int(idx[0])
-    checks = {}
+    checks = {} if oracle is not None else None
     ok = True
-    for kind, l in picks.items():
+    for kind, l in (picks.items() if oracle is not None else ()):
         kc, vc = caches[l]
         errs, lerrs, refs = [], [], []
         for g in (0, HKV - 1):
@@ -1127,7 +1138,8 @@ def qwen_leg(args, stream):
             "speedup_vs_all_fa": round(t_allfa / t_routed, 3),
             "algorithmic_bytes": loop_bytes,
             "achieved_gbs": round(loop_bytes / t_routed / 1e9, 1),
-            "parity_last_step": checks, "parity_pass": bool(ok),
+            "parity_last_step": checks,
+            "parity_pass": bool(ok) if checks is not None else None,
         },
     }
     del caches, qd_all, kn_all, vn_all
@@ -1141,7 +1153,7 @@ def needle_parity(T, scale):
     import numpy as np
     import torch
 
-    import oracle
+    oracle = load_oracle()
     from sparse_attention_layerrouter_amd import _lib, synth
 
     dev = torch.device("cuda:0")
@@ -1180,7 +1192,7 @@ def cpu_baseline(args, qkv, route_np, T, scale, t_prefill_gpu):
     import numpy as np
     import torch
 
-    import oracle
+    oracle = load_oracle()
     from sparse_attention_layerrouter_amd import _lib
 
     q, k, v = qkv
@@ -1259,7 +1271,7 @@ def cpu_full(stream):
     import numpy as np
     import torch
 
-    import oracle
+    oracle = load_oracle()
     from sparse_attention_layerrouter_amd import _lib, synth
 
     dev = torch.device("cuda:0")

@@ -1,7 +1,8 @@
 """CPU oracle for Flux Attention's layer-routed hybrid attention.
 
 TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
-``cpu_baseline`` leg of ``bench.py`` may import this package; the product
+CPU-baseline leg of ``bench.py`` (the oracle's timing and the parity checks that
+reuse it, all behind ``bench.load_oracle``) may import this package; the product
 library never does.  The arithmetic lives in ``fa_oracle.c`` (plain C, fp64
 accumulation, exact two-pass softmax); this module only marshals numpy arrays
 into it with ctypes.

@@ -1,7 +1,7 @@
 """CPU oracle of the Triangle Attention branch.
 
-TEST INFRASTRUCTURE ONLY, like the rest of ``oracle/``: the tests and
-``bench.py``'s checks may import it, the product library never does.
+TEST INFRASTRUCTURE ONLY, like the rest of ``oracle/``: the tests and the
+CPU-baseline leg of ``bench.py`` may import it, the product library never does.
 
 The pages use TriangleMix's Triangle Attention (TA) as a sparse backend of the
 router: a block-level, fixed ("triangle") topology, training-free, for prefill

@@ -1,7 +1,7 @@
 """CPU oracle of the XAttention sparse branch (antidiagonal block scoring).
 
-TEST INFRASTRUCTURE ONLY, like the rest of ``oracle/``: the tests and
-``bench.py``'s checks may import it, the product library never does.
+TEST INFRASTRUCTURE ONLY, like the rest of ``oracle/``: the tests and the
+CPU-baseline leg of ``bench.py`` may import it, the product library never does.
 
 The pages name XAttention as one of the sparse operators Flux Attention's
 router can send a layer to: "XAttention: Block Sparse Attention with
