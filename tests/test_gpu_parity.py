@@ -162,6 +162,7 @@ PREFILL_CASES = [
     ([390], 16, 2, 128, [0], 128, 128, 64),         # G = 8
     ([450, 129], 8, 2, 64, [1, 0], 64, 192, 64),    # d = 64
     ([300], 6, 2, 128, [0], 32, 64, 32),            # G = 3: plain kernel
+    ([260, 77], 32, 2, 128, [0, 1], 64, 128, 64),   # G = 16: four head groups per KV head
 ]
 
 
@@ -286,6 +287,8 @@ DECODE_CASES = [
     (2, 16, 2, 128, 900, [900, 31], [1, 0], 0, 128, 128, True),
     (2, 8, 2, 128, 600, [600, 250], [0, 1], 64, 128, 32, False),
     (1, 4, 2, 64, 256, [256], [0], 16, 64, 16, False),
+    (2, 32, 2, 128, 1500, [1500, 700], [1, 0], 128, 512, 64, True),   # G = 16
+    (2, 8, 4, 64, 900, [900, 450], [0, 1], 64, 256, 32, True),        # G = 2, d = 64
 ]
 
 
