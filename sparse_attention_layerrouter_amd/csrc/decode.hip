@@ -549,76 +549,64 @@ __global__ __launch_bounds__(kThreads, ONE ? 5 : 2) void decode_bf16_kernel(
 }
 
 // o[b][h] = sum_s e^{lse_s - M} o_s / sum_s e^{lse_s - M}, M = max_s lse_s.
-// One workgroup per (sequence, query head); the max and the weight sum are
-// block reductions in a fixed tree, the weighted sum runs in ascending s per
-// output element, so the result does not depend on timing.
-constexpr int kMergeThreads = 128;
-constexpr int kMergeChunk = 1024;
+// One workgroup per (sequence, query head), one thread per output element d.
+// Each wave handles the splits 64 at a time: lane s holds split s's lse and
+// weight, the max and the weight sum are fixed DPP / swizzle / permlane trees
+// (no LDS, no barrier), and every thread requests its 64 o partials of the chunk
+// (at clamped addresses, without branches) together with the lse values, so one
+// memory round trip feeds the whole chunk.  The weighted sum runs in ascending
+// s with the weight read from its lane, so the result does not depend on timing.
+__device__ __forceinline__ float wave_max(float x) { return max_xor32(group_max<32>(x)); }
+__device__ __forceinline__ float wave_sum(float x) { return sum_xor32(group_sum<32>(x)); }
 
-__device__ __forceinline__ float block_reduce(float v, float *red, bool is_max)
-{
-    const int tid = threadIdx.x;
-    red[tid] = v;
-    __syncthreads();
-    for (int off = kMergeThreads / 2; off > 0; off >>= 1) {
-        if (tid < off) red[tid] = is_max ? fmaxf(red[tid], red[tid + off]) : red[tid] + red[tid + off];
-        __syncthreads();
-    }
-    const float r = red[0];
-    __syncthreads();
-    return r;
-}
-
-template <typename TE>
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
+template <typename TE, int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(
     const float *__restrict__ o_part, const float *__restrict__ lse_part,
-    const int32_t *__restrict__ cache_len, int max_cache, int hq, int D, int n_splits,
+    const int32_t *__restrict__ cache_len, int max_cache, int hq, int n_splits,
     TE *__restrict__ o, float *__restrict__ lse)
 {
-    __shared__ float red[kMergeThreads];
-    __shared__ float wts[kMergeChunk];
+    static_assert(D % 64 == 0, "whole waves");
     const int bh = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int d = threadIdx.x;
+    const int lane = d & 63;
+    const float *lp = lse_part + (size_t)bh * n_splits;
+    const float *op = o_part + (size_t)bh * n_splits * D + d;
+
+    // the first chunk's partials are requested before the lse values are even
+    // reduced: they do not depend on them
+    float x[64];
+    {
+        const int cnt = min(64, n_splits);
+#pragma unroll
+        for (int u = 0; u < 64; ++u) x[u] = op[(size_t)min(u, cnt - 1) * D];
+    }
+    float m = -INFINITY;
+    for (int s = lane; s < n_splits; s += 64) m = fmaxf(m, lp[s]);
+    const float M = wave_max(m);
+    const float Mu = M == -INFINITY ? 0.0f : M;
+    float W = 0.0f, acc = 0.0f;
+    for (int s0 = 0; s0 < n_splits; s0 += 64) {
+        const int cnt = min(64, n_splits - s0);
+        if (s0 > 0) {  // caches of more than 64 splits
+#pragma unroll
+            for (int u = 0; u < 64; ++u) x[u] = op[(size_t)(s0 + min(u, cnt - 1)) * D];
+        }
+        const float ls = lane < cnt ? lp[s0 + lane] : -INFINITY;
+        const float w = ls == -INFINITY ? 0.0f : __expf(ls - Mu);
+        W += wave_sum(w);
+#pragma unroll
+        for (int u = 0; u < 64; ++u)
+            acc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u)) *
+                   x[u];
+    }
     const int n = cache_len[bh / hq];
     const bool bad = n < 1 || n > max_cache;  // max_cache: INT_MAX for ring caches
-    const float *lp = lse_part + (size_t)bh * n_splits;
-
-    float m = -INFINITY;
-    for (int s = tid; s < n_splits; s += kMergeThreads) m = fmaxf(m, lp[s]);
-    const float M = block_reduce(m, red, true);
-    float w = 0.0f;
-    for (int s = tid; s < n_splits; s += kMergeThreads)
-        w += lp[s] == -INFINITY ? 0.0f : __expf(lp[s] - M);
-    const float W = block_reduce(w, red, false);
-
-    float acc = 0.0f;
-    const float *op = o_part + (size_t)bh * n_splits * D + tid;
-    for (int s0 = 0; s0 < n_splits; s0 += kMergeChunk) {
-        const int cnt = min(kMergeChunk, n_splits - s0);
-        for (int s = tid; s < cnt; s += kMergeThreads)
-            wts[s] = lp[s0 + s] == -INFINITY ? 0.0f : __expf(lp[s0 + s] - M);
-        __syncthreads();
-        if (tid < D) {
-            int s = 0;
-            for (; s + 8 <= cnt; s += 8) {
-                float x[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) x[u] = op[(size_t)(s0 + s + u) * D];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) acc += wts[s + u] * x[u];
-            }
-            for (; s < cnt; ++s) acc += wts[s] * op[(size_t)(s0 + s) * D];
-        }
-        __syncthreads();
-    }
-    if (tid < D) {
-        const float val = bad ? __builtin_nanf("") : acc / W;
-        if constexpr (sizeof(TE) == 2)
-            ((uint16_t *)o)[(size_t)bh * D + tid] = to_bf16(val);
-        else
-            ((float *)o)[(size_t)bh * D + tid] = val;
-    }
-    if (lse && tid == 0) lse[bh] = bad ? __builtin_nanf("") : M + __logf(W);
+    const float val = bad ? __builtin_nanf("") : acc / W;
+    if constexpr (sizeof(TE) == 2)
+        ((uint16_t *)o)[(size_t)bh * D + d] = to_bf16(val);
+    else
+        ((float *)o)[(size_t)bh * D + d] = val;
+    if (lse && d == 0) lse[bh] = bad ? __builtin_nanf("") : M + __logf(W);
 }
 
 template <typename TE, int D, int G>
@@ -719,14 +707,17 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
                        : launch_by_g<float, 64>(a, stream, r, scale_log2);
     if (e != hipSuccess) return e;
     const int max_len = a.ring ? 0x7fffffff : a.max_cache;
-    if (a.bf16)
-        decode_merge_kernel<uint16_t><<<a.batch * a.hq, kMergeThreads, 0, stream>>>(
-            a.o_part, a.lse_part, a.cache_len, max_len, a.hq, a.d, a.n_splits, (uint16_t *)a.o,
-            a.lse);
-    else
-        decode_merge_kernel<float><<<a.batch * a.hq, kMergeThreads, 0, stream>>>(
-            a.o_part, a.lse_part, a.cache_len, max_len, a.hq, a.d, a.n_splits, (float *)a.o,
-            a.lse);
+#define FA_MERGE(TE, DD)                                                                      \
+    decode_merge_kernel<TE, DD><<<a.batch * a.hq, DD, 0, stream>>>(                            \
+        a.o_part, a.lse_part, a.cache_len, max_len, a.hq, a.n_splits, (TE *)a.o, a.lse)
+    if (a.bf16) {
+        if (a.d == 128) FA_MERGE(uint16_t, 128);
+        else FA_MERGE(uint16_t, 64);
+    } else {
+        if (a.d == 128) FA_MERGE(float, 128);
+        else FA_MERGE(float, 64);
+    }
+#undef FA_MERGE
     return hipGetLastError();
 }
 
