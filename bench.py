@@ -71,6 +71,9 @@ def parse():
                    help="run only the Qwen3-4B-shaped varlen leg (prefill + decode loop)")
     p.add_argument("--qwen-steps", type=int, default=256,
                    help="decode steps per sequence in the Qwen3-4B leg (each appends a token)")
+    p.add_argument("--no-clock", action="store_true",
+                   help="skip the graphics-clock window (e.g. under a profiler, whose "
+                        "environment the amd-smi child would inherit)")
     p.add_argument("--cpu-full", action="store_true",
                    help="only the unsampled oracle timings (tiny case, one SA layer at 32K, one "
                         "FA and one SA decode layer at batch 8 x 131072), with full-row parity")
@@ -400,7 +403,10 @@ def main():
     # own so that the sampling process cannot disturb the timed steps
     fa_route = torch.ones((1, N_LAYERS), dtype=torch.uint8, device=dev)
     fa_route_np = fa_route.cpu().numpy()
-    clocks = ClockSampler().start()
+    clocks = ClockSampler()
+    if args.no_clock:
+        clocks.exe = None
+    clocks.start()
     for i in range(24 if clocks.exe else 0):
         qs, ks, vs = sets[i % n_sets]
         _lib.fa_attn_prefill(qs, ks, vs, o_pre, cu, T, fa_route, 0, SINK, WINDOW, BLOCK, scale,

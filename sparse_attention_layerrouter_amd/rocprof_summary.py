@@ -3,6 +3,11 @@
     python -m sparse_attention_layerrouter_amd.rocprof_summary stats DIR
         per-kernel launch count and average / min / max duration from the
         *kernel_stats.csv (and *kernel_trace.csv) files rocprofv3 wrote in DIR.
+    python -m sparse_attention_layerrouter_amd.rocprof_summary grids DIR NAME_SUBSTRING
+        for the kernels whose name contains NAME_SUBSTRING: launch count and
+        average / min / max duration per grid size, from the *kernel_trace.csv
+        files (a kernel launched at several problem sizes in one run, e.g. the
+        131072-token FA prefill layer beside the context sweep's).
     python -m sparse_attention_layerrouter_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR \\
             COPY_FETCH_DIR COPY_WRITE_DIR OUT_JSON
         HBM bytes per launch of the hot kernels from FETCH_SIZE / WRITE_SIZE
@@ -67,6 +72,26 @@ def stats(directory):
         lines.append(f"{int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>11.2f} "
                      f"{float(r['MinNs']) / 1e3:>11.2f} {float(r['MaxNs']) / 1e3:>11.2f} "
                      f"{float(r['Percentage']):>8.2f}  {r['Name'][:150]}")
+    return "\n".join(lines)
+
+
+def grids(directory, needle):
+    """Per grid size of the kernels matching `needle`: launches and durations."""
+    acc = {}
+    for r in _rows(directory, "kernel_trace.csv"):
+        if needle not in r["Kernel_Name"]:
+            continue
+        key = (int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]),
+               int(r["Workgroup_Size_X"]))
+        dur = (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3
+        acc.setdefault(key, []).append(dur)
+    if not acc:
+        raise SystemExit(f"no launch of a kernel matching {needle!r} under {directory}")
+    lines = [f"{'calls':>6} {'avg_us':>11} {'min_us':>11} {'max_us':>11}  grid (x, y, z) threads, "
+             f"workgroup size  [{needle}]"]
+    for key, v in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{len(v):>6} {sum(v) / len(v):>11.2f} {min(v):>11.2f} {max(v):>11.2f}  "
+                     f"({key[0]}, {key[1]}, {key[2]}), {key[3]}")
     return "\n".join(lines)
 
 
@@ -199,6 +224,8 @@ def counters(directories, profile_json, out_json):
 if __name__ == "__main__":
     if len(sys.argv) >= 3 and sys.argv[1] == "stats":
         print(stats(sys.argv[2]))
+    elif len(sys.argv) == 4 and sys.argv[1] == "grids":
+        print(grids(sys.argv[2], sys.argv[3]))
     elif len(sys.argv) == 7 and sys.argv[1] == "traffic":
         print(json.dumps(traffic(*sys.argv[2:7]), indent=1))
     elif len(sys.argv) >= 5 and sys.argv[1] == "counters":
