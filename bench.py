@@ -25,7 +25,6 @@ Prints ONE JSON line.  `--gpus` above 1 is refused: this path runs on one GPU.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
