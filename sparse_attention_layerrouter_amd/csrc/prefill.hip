@@ -336,20 +336,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     TileLoader<D, true> lv;
     lk.init(wq, lane, row_stride);
     lv.init(wq, lane, row_stride);
-    // Clear the tile buffers once: a copy past the sequence end may leave rows
-    // unwritten, and the first MFMA block multiplies a zero P with v_lds1; both
-    // then see zeros, never stale bit patterns.
-    for (int i = tid; i < TILE_BYTES / 16; i += kThreads) {
-        *(u32x4 *)(k_lds0 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
-        *(u32x4 *)(k_lds1 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
-        *(u32x4 *)(v_lds0 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
-        *(u32x4 *)(v_lds1 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
-    }
-    __syncthreads();
+    // The first K tile is requested at once.  The V buffers are cleared once: a
+    // copy past the sequence end may leave rows unwritten, and P = 0 times a
+    // stale NaN pattern would still be NaN (the first MFMA block multiplies a zero
+    // P with v_lds1).  K rows past the end need no clearing: their scores are
+    // masked to -inf whatever they hold.  The clear is complete before the first
+    // phase barrier (which waits for every wave's LDS accesses).
     if (grp == 0) {
         const __amdgpu_buffer_rsrc_t r0 = lk.rsrc(kb, row_stride, tile_k0(0), T);
 #pragma unroll
         for (int i = 0; i < lk.NI; ++i) lk.issue_one(i, k_lds0, r0);
+    }
+    for (int i = tid; i < TILE_BYTES / 16; i += kThreads) {
+        *(u32x4 *)(v_lds0 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+        *(u32x4 *)(v_lds1 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
     }
 
     // ---- Q^T operand in registers: lane holds row pw0 + l32, d = ks*16 + half*8 ..
@@ -453,8 +453,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     // When LD is set (group 0 at even phases 2j) the block also issues the
     // copies of K of tile j+1 and V of tile j, one every 4 MFMAs, so the memory
     // pipeline drains while the matrix cores work and group 1's softmax is not
-    // interrupted.  Past the last tile the copies repeat the last tile into
-    // buffers nobody reads again.
+    // interrupted.  Past the last tile the copies have an empty range (their
+    // buffers are not read again).
     auto block_mfma = [&](auto ld_tag, const char *k_lds, const char *v_lds, int t, char *kdst,
                           char *vdst) __attribute__((always_inline)) {
         constexpr bool LD = decltype(ld_tag)::value != 0;
@@ -471,8 +471,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         s_live = t < n_tiles && wave_sees(k0_t, ent);
         __amdgpu_buffer_rsrc_t rk, rv;
         if constexpr (LD) {
-            rk = lk.rsrc(kb, row_stride, tile_k0(min(t + 1, n_tiles - 1)), T);
-            rv = lv.rsrc(vb, row_stride, k0_t, T);
+            // past the last tile the copies get an empty range: they move no data
+            // (nobody reads those buffers again) and the workgroup's final wait
+            // for them is short
+            rk = lk.rsrc(kb, row_stride, tile_k0(min(t + 1, n_tiles - 1)), t + 1 < n_tiles ? T : 0);
+            rv = lv.rsrc(vb, row_stride, k0_t, t < n_tiles ? T : 0);
         }
         s[0] = f32x16{};
         s[1] = f32x16{};
