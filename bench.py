@@ -81,6 +81,11 @@ def parse():
     p.add_argument("--profile", action="store_true",
                    help="short kernel-only run for rocprofv3 counter passes: one FA and one "
                         "SA prefill layer and one FA and one SA decode layer, twice")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the ceiling streams (plain read, MFMA + LDS + softmax-mix "
+                        "streams) timed before the inputs are allocated")
+    p.add_argument("--only-ceilings", action="store_true",
+                   help="run only the ceiling streams and print them")
     p.add_argument("--copy-probe", action="store_true",
                    help="only a plain 1 GiB read + 1 GiB write elementwise kernel (counter "
                         "calibration)")
@@ -278,6 +283,12 @@ def main():
         print(json.dumps({"copy_probe_bytes_each_way": x.numel() * 4}))
         return
     stream = torch.cuda.current_stream()
+    ceil = None
+    if args.only_ceilings or not (args.no_ceilings or args.profile):
+        ceil = ceilings_leg(stream)
+        if args.only_ceilings:
+            print(json.dumps({"ceilings": ceil}))
+            return
     if args.only_qwen:
         print(json.dumps({"qwen3_4b_varlen": qwen_leg(args, stream)}))
         return
@@ -864,6 +875,11 @@ def main():
             "traffic": read_traffic("decode_bf16_fa_131k", dec_hash),
         },
     }
+    if ceil is not None:
+        ceil["fa_prefill_over_softmax_mix_stream"] = round(
+            achieved_tflops / ceil["mix"]["softmax_mix_1_read_tflops"], 4)
+        ceil["fa_decode_over_read_stream"] = round(achieved_gbs / ceil["read"]["best_gbs"], 4)
+        result["ceilings"] = ceil
 
     # ---- CPU oracle baseline (rank 0, N=1 only) and sampled parity -------------
     if not args.no_cpu_baseline:
@@ -929,6 +945,29 @@ def _time_calls(stream, fn, warmup, timed):
         evs.append((a, b))
     torch.cuda.synchronize()
     return [a.elapsed_time(b) for a, b in evs]
+
+
+def ceilings_leg(stream):
+    """Measured ceilings of this board for the two hot kernels' mixes: a plain
+    non-temporal read of 4 GiB (the FA decode layer's K/V bytes at batch 8 x
+    131072) at three workgroup chunk sizes, and dependence-free streams of
+    32x32x16 bf16 products (8 waves per CU) with 0, 1/2, 3/4 or 1 LDS operand
+    read of 1 KiB per product, without and with the online softmax's VALU mix
+    (one exponential, one FMA, one add and half a bf16 pair pack per product;
+    the FA prefill kernel issues one exponential and about 2.6 other VALU
+    instructions and 1 KiB of LDS reads per product)."""
+    from sparse_attention_layerrouter_amd import ceilings
+
+    ceilings.lib()
+    log("ceiling streams: read")
+    rd = ceilings.measure_read(stream)
+    log("ceiling streams: matrix products")
+    mx = ceilings.measure_mix(stream)
+    one = [r for r in mx["streams"] if r["softmax_mix"] and r["lds_reads_per_product"] == 1.0]
+    pure = [r for r in mx["streams"] if not r["softmax_mix"] and r["lds_reads_per_product"] == 0]
+    mx["softmax_mix_1_read_tflops"] = one[0]["tflops"]
+    mx["products_only_tflops"] = pure[0]["tflops"]
+    return {"read": rd, "mix": mx}
 
 
 def config2_leg(stream, qkv):

@@ -1,8 +1,10 @@
 """Build libfluxattn.so (the C-ABI library of include/fluxattn.h) for gfx950.
 
-Every HIP source under csrc/ and the host ABI (csrc/api.cpp) is compiled with
-hipcc for gfx950 only and linked in-tree into
-sparse_attention_layerrouter_amd/libfluxattn.so.
+Every attention HIP source under csrc/ and the host ABI (csrc/api.cpp) is
+compiled with hipcc for gfx950 only and linked in-tree into
+sparse_attention_layerrouter_amd/libfluxattn.so.  The ceiling kernels
+(csrc/ceilings.hip, measuring instruments of the benchmark, not part of the
+attention path) are linked into a library of their own, libfa_ceilings.so.
 
     python -m sparse_attention_layerrouter_amd.build
 """
@@ -20,6 +22,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libfluxattn.so")
+CEILINGS_OUT = os.path.join(PKG, "libfa_ceilings.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -32,6 +35,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 SOURCES = ["router.hip", "prefill.hip", "decode.hip", "xattn.hip", "api.cpp"]
+CEILINGS_SOURCE = "ceilings.hip"
 # The hot MFMA / split-K kernels keep everything in registers: a build whose
 # compiler places any of their state in scratch memory (spills or a stack
 # array) is refused, since it would run many times slower.
@@ -76,23 +80,29 @@ def check_resources(res: dict) -> None:
         raise RuntimeError("hot kernels would use scratch memory:\n  " + "\n  ".join(bad))
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        done = list(ex.map(_compile, SOURCES))
-    objs = [o for o, _ in done]
-    res = {k: v for _, r in done for k, v in r.items()}
-    with open(os.path.join(BUILD_DIR, "kernel_resources.json"), "w") as f:
-        json.dump(res, f, indent=1, sort_keys=True)
-    check_resources(res)
-    tmp = OUT + ".tmp"
+def _link(objs: list, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + [CEILINGS_SOURCE]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        done = dict(zip(srcs, ex.map(_compile, srcs)))
+    res = {k: v for src in SOURCES for k, v in done[src][1].items()}
+    with open(os.path.join(BUILD_DIR, "kernel_resources.json"), "w") as f:
+        json.dump(res, f, indent=1, sort_keys=True)
+    check_resources(res)
+    _link([done[src][0] for src in SOURCES], OUT)
+    _link([done[CEILINGS_SOURCE][0]], CEILINGS_OUT)
     if verbose:
         print(f"built {OUT}")
+        print(f"built {CEILINGS_OUT}")
     return OUT
 
 

@@ -1,0 +1,146 @@
+"""ctypes binding and timing of libfa_ceilings.so (csrc/ceilings.hip).
+
+The ceiling kernels are measuring instruments of the benchmark, not part of
+the attention path: a plain non-temporal read stream (the rate a read of N
+bytes reaches on this board) and a dependence-free stream of 32x32x16 bf16
+matrix products with a chosen LDS operand read rate and an optional
+online-softmax VALU mix (the rate that mix reaches under the board's power
+limit).  The functions below marshal arguments and time launches with HIP
+events on the given stream; the kernels do the work.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa_ceilings.so")
+EXPORTS = ("fa_ceiling_last_error", "fa_ceiling_read", "fa_ceiling_mix")
+
+MIX_THREADS = 512
+MIX_WAVES = 8
+MIX_PRODUCTS = 8              # products per wave per iteration
+MIX_PRODUCT_FLOP = 32 * 32 * 16 * 2
+READ_THREADS = 256
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m sparse_attention_layerrouter_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.fa_ceiling_last_error.restype = ctypes.c_char_p
+    L.fa_ceiling_last_error.argtypes = []
+    L.fa_ceiling_read.restype = I32
+    L.fa_ceiling_read.argtypes = [P, SZ, SZ, P, P]
+    L.fa_ceiling_mix.restype = I32
+    L.fa_ceiling_mix.argtypes = [I32, I32, I32, I32, P, P, P]
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = lib().fa_ceiling_last_error().decode()
+        raise RuntimeError(f"ceiling kernel: status {status}: {msg}")
+
+
+def _stream_ptr(stream):
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def fa_ceiling_read(buf, chunk: int, sink, stream=None) -> None:
+    """Read every byte of buf (a device tensor) once, chunk bytes per workgroup;
+    sink (device uint32 / int32, (nbytes / chunk) * 256 entries) receives each
+    thread's XOR of the 32-bit words it read."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().fa_ceiling_read(ctypes.c_void_p(buf.data_ptr()), nbytes, chunk,
+                                 ctypes.c_void_p(sink.data_ptr()), _stream_ptr(stream)))
+
+
+def fa_ceiling_mix(reads_per_8: int, softmax: bool, n_workgroups: int, iterations: int,
+                   seed, out, stream=None) -> None:
+    """One launch of the product stream: n_workgroups x 8 waves x iterations x 8
+    products; seed is an 8 KiB device buffer, out n_workgroups * 512 floats."""
+    _check(lib().fa_ceiling_mix(reads_per_8, 1 if softmax else 0, n_workgroups, iterations,
+                                ctypes.c_void_p(seed.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                _stream_ptr(stream)))
+
+
+def mix_flop(n_workgroups: int, iterations: int) -> float:
+    return float(n_workgroups) * MIX_WAVES * iterations * MIX_PRODUCTS * MIX_PRODUCT_FLOP
+
+
+def _time_ms(fn, stream, reps: int) -> list:
+    import torch
+
+    fn()  # warm-up
+    out = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        out.append(a.elapsed_time(b))
+    return out
+
+
+def measure_read(stream, nbytes: int = 1 << 32, chunks=(128 << 10, 1 << 20, 4 << 20),
+                 reps: int = 5) -> dict:
+    """Read rate of an nbytes buffer at each chunk size (best of reps, GB/s)."""
+    import torch
+
+    dev = torch.device("cuda", torch.cuda.current_device())
+    with torch.cuda.stream(stream):
+        buf = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).random_()
+        sink = torch.empty(nbytes // min(chunks) * READ_THREADS, dtype=torch.int32, device=dev)
+    res = {}
+    for c in chunks:
+        ts = _time_ms(lambda: fa_ceiling_read(buf, c, sink, stream), stream, reps)
+        best = min(ts)
+        res[f"{c >> 10}KiB"] = {"ms_best": round(best, 4), "gbs": round(nbytes / best / 1e6, 1)}
+    del buf, sink
+    torch.cuda.synchronize()
+    return {"bytes": nbytes, "workgroup_threads": READ_THREADS, "by_chunk": res,
+            "best_gbs": max(v["gbs"] for v in res.values())}
+
+
+def measure_mix(stream, configs=((0, False), (8, False), (6, False), (4, False),
+                                 (0, True), (8, True), (6, True), (4, True)),
+                n_workgroups: int = 1024, iterations: int = 40000, reps: int = 3) -> dict:
+    """TFLOP/s of the product stream for each (LDS reads per 8 products,
+    softmax mix) pair (median of reps launches of about 40-60 ms each)."""
+    import numpy as np
+    import torch
+
+    dev = torch.device("cuda", torch.cuda.current_device())
+    # bf16 operand values of magnitude 2^-4 .. 2^-3 with random signs and mantissas
+    rng = np.random.default_rng(1)
+    expo = 123 + rng.integers(0, 2, 4096)  # biased exponents of 2^-4 and 2^-3
+    bits = ((rng.integers(0, 2, 4096) << 15) | (expo << 7) | rng.integers(0, 128, 4096)).astype(
+        np.uint16)
+    with torch.cuda.stream(stream):
+        seed = torch.from_numpy(bits.view(np.int16)).to(dev)
+        out = torch.empty(n_workgroups * MIX_THREADS, dtype=torch.float32, device=dev)
+    flop = mix_flop(n_workgroups, iterations)
+    res = []
+    for rd, sm in configs:
+        ts = sorted(_time_ms(lambda: fa_ceiling_mix(rd, sm, n_workgroups, iterations, seed, out,
+                                                    stream), stream, reps))
+        med = ts[len(ts) // 2]
+        res.append({"lds_reads_per_product": rd / 8, "softmax_mix": bool(sm),
+                    "ms": round(med, 3), "tflops": round(flop / med / 1e9, 1)})
+    torch.cuda.synchronize()
+    return {"workgroups": n_workgroups, "iterations": iterations,
+            "flop_per_launch": flop, "streams": res}

@@ -1,0 +1,198 @@
+// Ceiling kernels: what plain instruction streams reach on this board, as the
+// measured context of the attention kernels' roofline fractions.
+//
+// These are measuring instruments, not part of the attention path: they are
+// built into their own library (libfa_ceilings.so) and only the benchmark and
+// its tests call them.
+//
+//  * fa_ceiling_read streams a device buffer: each 256-thread workgroup reads
+//    one contiguous chunk with 16-byte non-temporal loads, eight in flight per
+//    lane (the access pattern of the decode kernels' K/V reads).  Its rate is
+//    what a plain read of that many bytes reaches, against the 8 TB/s HBM peak.
+//  * fa_ceiling_mix issues 32x32x16 bf16 matrix products from 8 waves per CU
+//    (two per SIMD, one workgroup per CU, like the prefill kernel), with a
+//    chosen number of 1 KiB LDS operand reads per product and, optionally, an
+//    online-softmax-like VALU mix per product: one exponential, one FMA, one
+//    add and half of a bf16 pair pack with its consumer.  The board runs such
+//    work at a power-limited clock, so the matrix cores' rate depends on what
+//    else the CU issues; this stream has no dependences between the three
+//    kinds of work, no barriers and no global traffic, so it is the rate that
+//    a kernel with the same mix can reach at best.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstddef>
+#include <cstdint>
+#include <cstdio>
+
+extern "C" {
+const char *fa_ceiling_last_error(void);
+int fa_ceiling_read(const void *buf, size_t bytes, size_t chunk, uint32_t *sink,
+                    hipStream_t stream);
+int fa_ceiling_mix(int reads_per_8, int softmax, int n_workgroups, int iterations,
+                   const void *seed, float *out, hipStream_t stream);
+}
+
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+thread_local char g_err[256] = "";
+
+int fail(int code, const char *msg) {
+    snprintf(g_err, sizeof g_err, "%s", msg);
+    return code;
+}
+
+constexpr int kReadThreads = 256;
+constexpr int kReadInFlight = 8;
+constexpr size_t kReadGranule = (size_t)16 * kReadThreads * kReadInFlight;  // 32 KiB
+
+// One workgroup per chunk of chunk16 16-byte words; chunk16 is a multiple of
+// kReadThreads * kReadInFlight, so every load is inside the workgroup's chunk.
+// Each thread writes the XOR of the 32-bit words it read, so the loads are
+// kept and the XOR of all sink words is the XOR of the whole buffer.
+__global__ __launch_bounds__(kReadThreads) void ceiling_read_kernel(
+    const u32x4 *__restrict__ p, size_t chunk16, uint32_t *__restrict__ sink) {
+    const u32x4 *base = p + (size_t)blockIdx.x * chunk16 + threadIdx.x;
+    uint32_t acc = 0;
+    for (size_t i = 0; i < chunk16; i += (size_t)kReadThreads * kReadInFlight) {
+        u32x4 v[kReadInFlight];
+#pragma unroll
+        for (int u = 0; u < kReadInFlight; ++u)
+            v[u] = __builtin_nontemporal_load(base + i + (size_t)u * kReadThreads);
+#pragma unroll
+        for (int u = 0; u < kReadInFlight; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    sink[(size_t)blockIdx.x * kReadThreads + threadIdx.x] = acc;
+}
+
+constexpr int kMixThreads = 512;
+constexpr int kSeedWords = 512;      // 16-byte words of the seed buffer (8 KiB)
+constexpr int kLdsWords = 6144;      // 96 KiB: one workgroup per CU, as the prefill kernel
+constexpr int kMixProducts = 8;      // independent accumulators per wave
+
+// Per iteration each wave issues 8 products into 8 accumulators; the first RD of
+// them take their A operand from a fresh 16-byte-per-lane LDS read (1 KiB per
+// wave), the others from a register.  The read rows move with the iteration
+// (16 sets), so operand values change and no read is loop-invariant.  With SM
+// every product is paired with x = x * 0.5 - 0.25 (FMA), e = 2^x, s += e, and
+// every second product with a bf16 pair conversion of two e's folded into a
+// running XOR.
+template <int RD, bool SM>
+__global__ __launch_bounds__(kMixThreads, 1) void ceiling_mix_kernel(
+    const u32x4 *__restrict__ seed, float *__restrict__ out, int iterations) {
+    __shared__ u32x4 lds[kLdsWords];
+    for (int i = threadIdx.x; i < kLdsWords; i += kMixThreads) lds[i] = seed[i & (kSeedWords - 1)];
+    __syncthreads();
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const bf16x8 b = __builtin_bit_cast(bf16x8, seed[(threadIdx.x + 7) & (kSeedWords - 1)]);
+    const bf16x8 a_reg = __builtin_bit_cast(bf16x8, seed[(threadIdx.x + 3) & (kSeedWords - 1)]);
+    f32x16 c[kMixProducts];
+#pragma unroll
+    for (int i = 0; i < kMixProducts; ++i) c[i] = f32x16{};
+    float x[kMixProducts], s[kMixProducts];
+#pragma unroll
+    for (int i = 0; i < kMixProducts; ++i) {
+        x[i] = 0.001f * (float)(threadIdx.x + i);
+        s[i] = 0.0f;
+    }
+    uint32_t pk = 0;
+    for (int it = 0; it < iterations; ++it) {
+        // rows wave * 64 + lane + 64 (it mod 16) + 512 i: at most 511 + 960 + 3584 < kLdsWords
+        const u32x4 *set = lds + wave * 64 + lane + 64 * (it & 15);
+        bf16x8 a[kMixProducts];
+#pragma unroll
+        for (int i = 0; i < kMixProducts; ++i)
+            a[i] = i < RD ? __builtin_bit_cast(bf16x8, set[512 * i]) : a_reg;
+#pragma unroll
+        for (int i = 0; i < kMixProducts; ++i)
+            c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, c[i], 0, 0, 0);
+        if constexpr (SM) {
+            float e[kMixProducts];
+#pragma unroll
+            for (int i = 0; i < kMixProducts; ++i) {
+                x[i] = x[i] * 0.5f - 0.25f;
+                e[i] = __builtin_amdgcn_exp2f(x[i]);
+                s[i] += e[i];
+            }
+#pragma unroll
+            for (int i = 0; i < kMixProducts; i += 2) {
+                const bf16x2 pair = {(__bf16)e[i], (__bf16)e[i + 1]};
+                pk ^= __builtin_bit_cast(uint32_t, pair);
+            }
+        }
+    }
+    float r = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMixProducts; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) r += c[i][j];
+#pragma unroll
+    for (int i = 0; i < kMixProducts; ++i) r += s[i];
+    r += (float)(pk & 1u);
+    // one LDS word in the result keeps the 96 KiB allocation (one workgroup
+    // per CU) also in the variants without operand reads
+    r += (float)(lds[threadIdx.x].x & 1u);
+    out[(size_t)blockIdx.x * kMixThreads + threadIdx.x] = r;
+}
+
+template <int RD>
+void launch_mix(bool sm, int n_wg, int iterations, const u32x4 *seed, float *out, hipStream_t st) {
+    if (sm)
+        ceiling_mix_kernel<RD, true><<<n_wg, kMixThreads, 0, st>>>(seed, out, iterations);
+    else
+        ceiling_mix_kernel<RD, false><<<n_wg, kMixThreads, 0, st>>>(seed, out, iterations);
+}
+
+}  // namespace
+
+extern "C" const char *fa_ceiling_last_error(void) { return g_err; }
+
+// buf: device, bytes long, 16-byte aligned; chunk: bytes per workgroup, a
+// multiple of 32 KiB dividing bytes; sink: device, (bytes / chunk) * 256
+// uint32.  Returns 0, 1 for a bad argument, 4 for a HIP launch error.
+extern "C" int fa_ceiling_read(const void *buf, size_t bytes, size_t chunk, uint32_t *sink,
+                               hipStream_t stream) {
+    if (!buf || !sink) return fail(1, "fa_ceiling_read: null pointer");
+    if (((uintptr_t)buf & 15u) != 0) return fail(1, "fa_ceiling_read: buffer not 16-byte aligned");
+    if (chunk == 0 || chunk % kReadGranule != 0)
+        return fail(1, "fa_ceiling_read: chunk must be a positive multiple of 32 KiB");
+    if (bytes == 0 || bytes % chunk != 0) return fail(1, "fa_ceiling_read: chunk must divide bytes");
+    if (bytes / chunk > (size_t)INT_MAX) return fail(1, "fa_ceiling_read: too many chunks");
+    (void)hipGetLastError();
+    ceiling_read_kernel<<<(unsigned)(bytes / chunk), kReadThreads, 0, stream>>>(
+        (const u32x4 *)buf, chunk / 16, sink);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(4, hipGetErrorString(e));
+    return 0;
+}
+
+// reads_per_8: 0, 2, 4, 6 or 8 LDS operand reads per 8 products; softmax: 0
+// or 1; n_workgroups >= 1; iterations >= 1 (8 products per wave each);
+// seed: device, 8 KiB; out: device, n_workgroups * 512 floats.  Each launch
+// performs n_workgroups * 8 waves * iterations * 8 products of 32768 flop.
+extern "C" int fa_ceiling_mix(int reads_per_8, int softmax, int n_workgroups, int iterations,
+                              const void *seed, float *out, hipStream_t stream) {
+    if (!seed || !out) return fail(1, "fa_ceiling_mix: null pointer");
+    if (softmax != 0 && softmax != 1) return fail(1, "fa_ceiling_mix: softmax must be 0 or 1");
+    if (n_workgroups < 1) return fail(1, "fa_ceiling_mix: n_workgroups must be >= 1");
+    if (iterations < 1) return fail(1, "fa_ceiling_mix: iterations must be >= 1");
+    const u32x4 *sd = (const u32x4 *)seed;
+    const bool sm = softmax == 1;
+    (void)hipGetLastError();
+    switch (reads_per_8) {
+        case 0: launch_mix<0>(sm, n_workgroups, iterations, sd, out, stream); break;
+        case 2: launch_mix<2>(sm, n_workgroups, iterations, sd, out, stream); break;
+        case 4: launch_mix<4>(sm, n_workgroups, iterations, sd, out, stream); break;
+        case 6: launch_mix<6>(sm, n_workgroups, iterations, sd, out, stream); break;
+        case 8: launch_mix<8>(sm, n_workgroups, iterations, sd, out, stream); break;
+        default: return fail(1, "fa_ceiling_mix: reads_per_8 must be 0, 2, 4, 6 or 8");
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(4, hipGetErrorString(e));
+    return 0;
+}
