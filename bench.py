@@ -879,6 +879,9 @@ def main():
         ceil["fa_prefill_over_softmax_mix_stream"] = round(
             achieved_tflops / ceil["mix"]["softmax_mix_1_read_tflops"], 4)
         ceil["fa_decode_over_read_stream"] = round(achieved_gbs / ceil["read"]["best_gbs"], 4)
+        if xattn is not None:
+            ceil["xa_scores_iid_over_small_product_stream"] = round(
+                xattn["inputs"]["iid"]["scores_tflops"] / ceil["mix"]["small_1_read_tflops"], 4)
         result["ceilings"] = ceil
 
     # ---- CPU oracle baseline (rank 0, N=1 only) and sampled parity -------------
@@ -955,7 +958,9 @@ def ceilings_leg(stream):
     read of 1 KiB per product, without and with the online softmax's VALU mix
     (one exponential, one FMA, one add and half a bf16 pair pack per product;
     the FA prefill kernel issues one exponential and about 2.6 other VALU
-    instructions and 1 KiB of LDS reads per product)."""
+    instructions and 1 KiB of LDS reads per product), and 16x16x32 products
+    with 0 or 1 read per product (the XAttention score kernel's mix: one 1 KiB
+    read per 16x16x32 product and little VALU work)."""
     from sparse_attention_layerrouter_amd import ceilings
 
     ceilings.lib()
@@ -963,10 +968,14 @@ def ceilings_leg(stream):
     rd = ceilings.measure_read(stream)
     log("ceiling streams: matrix products")
     mx = ceilings.measure_mix(stream)
-    one = [r for r in mx["streams"] if r["softmax_mix"] and r["lds_reads_per_product"] == 1.0]
-    pure = [r for r in mx["streams"] if not r["softmax_mix"] and r["lds_reads_per_product"] == 0]
-    mx["softmax_mix_1_read_tflops"] = one[0]["tflops"]
-    mx["products_only_tflops"] = pure[0]["tflops"]
+
+    def pick(shape, reads, sm):
+        return [r for r in mx["streams"] if r["shape"] == shape and r["softmax_mix"] == sm
+                and r["lds_reads_per_product"] == reads][0]["tflops"]
+
+    mx["softmax_mix_1_read_tflops"] = pick("32x32x16", 1.0, True)
+    mx["products_only_tflops"] = pick("32x32x16", 0.0, False)
+    mx["small_1_read_tflops"] = pick("16x16x32", 1.0, False)
     return {"read": rd, "mix": mx}
 
 

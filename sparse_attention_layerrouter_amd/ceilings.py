@@ -20,7 +20,8 @@ EXPORTS = ("fa_ceiling_last_error", "fa_ceiling_read", "fa_ceiling_mix")
 MIX_THREADS = 512
 MIX_WAVES = 8
 MIX_PRODUCTS = 8              # products per wave per iteration
-MIX_PRODUCT_FLOP = 32 * 32 * 16 * 2
+MIX_PRODUCT_FLOP = {0: 32 * 32 * 16 * 2, 1: 16 * 16 * 32 * 2}  # by shape
+SHAPE_NAME = {0: "32x32x16", 1: "16x16x32"}
 READ_THREADS = 256
 
 _lib = None
@@ -40,7 +41,7 @@ def lib() -> ctypes.CDLL:
     L.fa_ceiling_read.restype = I32
     L.fa_ceiling_read.argtypes = [P, SZ, SZ, P, P]
     L.fa_ceiling_mix.restype = I32
-    L.fa_ceiling_mix.argtypes = [I32, I32, I32, I32, P, P, P]
+    L.fa_ceiling_mix.argtypes = [I32, I32, I32, I32, I32, P, P, P]
     _lib = L
     return L
 
@@ -68,16 +69,17 @@ def fa_ceiling_read(buf, chunk: int, sink, stream=None) -> None:
 
 
 def fa_ceiling_mix(reads_per_8: int, softmax: bool, n_workgroups: int, iterations: int,
-                   seed, out, stream=None) -> None:
+                   seed, out, stream=None, shape: int = 0) -> None:
     """One launch of the product stream: n_workgroups x 8 waves x iterations x 8
-    products; seed is an 8 KiB device buffer, out n_workgroups * 512 floats."""
-    _check(lib().fa_ceiling_mix(reads_per_8, 1 if softmax else 0, n_workgroups, iterations,
+    products (shape 0: 32x32x16, 1: 16x16x32); seed is an 8 KiB device buffer,
+    out n_workgroups * 512 floats."""
+    _check(lib().fa_ceiling_mix(reads_per_8, 1 if softmax else 0, shape, n_workgroups, iterations,
                                 ctypes.c_void_p(seed.data_ptr()), ctypes.c_void_p(out.data_ptr()),
                                 _stream_ptr(stream)))
 
 
-def mix_flop(n_workgroups: int, iterations: int) -> float:
-    return float(n_workgroups) * MIX_WAVES * iterations * MIX_PRODUCTS * MIX_PRODUCT_FLOP
+def mix_flop(n_workgroups: int, iterations: int, shape: int = 0) -> float:
+    return float(n_workgroups) * MIX_WAVES * iterations * MIX_PRODUCTS * MIX_PRODUCT_FLOP[shape]
 
 
 def _time_ms(fn, stream, reps: int) -> list:
@@ -116,11 +118,13 @@ def measure_read(stream, nbytes: int = 1 << 32, chunks=(128 << 10, 1 << 20, 4 <<
             "best_gbs": max(v["gbs"] for v in res.values())}
 
 
-def measure_mix(stream, configs=((0, False), (8, False), (6, False), (4, False),
-                                 (0, True), (8, True), (6, True), (4, True)),
+def measure_mix(stream, configs=((0, False, 0), (8, False, 0), (6, False, 0), (4, False, 0),
+                                 (0, True, 0), (8, True, 0), (6, True, 0), (4, True, 0),
+                                 (0, False, 1), (8, False, 1), (4, False, 1), (4, True, 1),
+                                 (8, True, 1)),
                 n_workgroups: int = 1024, iterations: int = 40000, reps: int = 3) -> dict:
     """TFLOP/s of the product stream for each (LDS reads per 8 products,
-    softmax mix) pair (median of reps launches of about 40-60 ms each)."""
+    softmax mix, shape) triple (median of reps launches of about 25-60 ms each)."""
     import numpy as np
     import torch
 
@@ -133,14 +137,14 @@ def measure_mix(stream, configs=((0, False), (8, False), (6, False), (4, False),
     with torch.cuda.stream(stream):
         seed = torch.from_numpy(bits.view(np.int16)).to(dev)
         out = torch.empty(n_workgroups * MIX_THREADS, dtype=torch.float32, device=dev)
-    flop = mix_flop(n_workgroups, iterations)
     res = []
-    for rd, sm in configs:
+    for rd, sm, shape in configs:
+        flop = mix_flop(n_workgroups, iterations, shape)
         ts = sorted(_time_ms(lambda: fa_ceiling_mix(rd, sm, n_workgroups, iterations, seed, out,
-                                                    stream), stream, reps))
+                                                    stream, shape), stream, reps))
         med = ts[len(ts) // 2]
-        res.append({"lds_reads_per_product": rd / 8, "softmax_mix": bool(sm),
-                    "ms": round(med, 3), "tflops": round(flop / med / 1e9, 1)})
+        res.append({"shape": SHAPE_NAME[shape], "lds_reads_per_product": rd / 8,
+                    "softmax_mix": bool(sm), "ms": round(med, 3),
+                    "tflops": round(flop / med / 1e9, 1)})
     torch.cuda.synchronize()
-    return {"workgroups": n_workgroups, "iterations": iterations,
-            "flop_per_launch": flop, "streams": res}
+    return {"workgroups": n_workgroups, "iterations": iterations, "streams": res}

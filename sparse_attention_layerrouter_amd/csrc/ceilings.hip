@@ -9,8 +9,9 @@
 //    one contiguous chunk with 16-byte non-temporal loads, eight in flight per
 //    lane (the access pattern of the decode kernels' K/V reads).  Its rate is
 //    what a plain read of that many bytes reaches, against the 8 TB/s HBM peak.
-//  * fa_ceiling_mix issues 32x32x16 bf16 matrix products from 8 waves per CU
-//    (two per SIMD, one workgroup per CU, like the prefill kernel), with a
+//  * fa_ceiling_mix issues 32x32x16 (or 16x16x32) bf16 matrix products from 8
+//    waves per CU (two per SIMD, one workgroup per CU, like the prefill and
+//    XAttention score kernels), with a
 //    chosen number of 1 KiB LDS operand reads per product and, optionally, an
 //    online-softmax-like VALU mix per product: one exponential, one FMA, one
 //    add and half of a bf16 pair pack with its consumer.  The board runs such
@@ -24,12 +25,13 @@
 #include <cstddef>
 #include <cstdint>
 #include <cstdio>
+#include <type_traits>
 
 extern "C" {
 const char *fa_ceiling_last_error(void);
 int fa_ceiling_read(const void *buf, size_t bytes, size_t chunk, uint32_t *sink,
                     hipStream_t stream);
-int fa_ceiling_mix(int reads_per_8, int softmax, int n_workgroups, int iterations,
+int fa_ceiling_mix(int reads_per_8, int softmax, int shape, int n_workgroups, int iterations,
                    const void *seed, float *out, hipStream_t stream);
 }
 
@@ -39,6 +41,7 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 thread_local char g_err[256] = "";
 
@@ -81,8 +84,9 @@ constexpr int kMixProducts = 8;      // independent accumulators per wave
 // (16 sets), so operand values change and no read is loop-invariant.  With SM
 // every product is paired with x = x * 0.5 - 0.25 (FMA), e = 2^x, s += e, and
 // every second product with a bf16 pair conversion of two e's folded into a
-// running XOR.
-template <int RD, bool SM>
+// running XOR (for 16x16x32 products, every second product: the same VALU
+// work per flop).
+template <int RD, bool SM, bool SMALL>
 __global__ __launch_bounds__(kMixThreads, 1) void ceiling_mix_kernel(
     const u32x4 *__restrict__ seed, float *__restrict__ out, int iterations) {
     __shared__ u32x4 lds[kLdsWords];
@@ -91,9 +95,10 @@ __global__ __launch_bounds__(kMixThreads, 1) void ceiling_mix_kernel(
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const bf16x8 b = __builtin_bit_cast(bf16x8, seed[(threadIdx.x + 7) & (kSeedWords - 1)]);
     const bf16x8 a_reg = __builtin_bit_cast(bf16x8, seed[(threadIdx.x + 3) & (kSeedWords - 1)]);
-    f32x16 c[kMixProducts];
+    typedef typename std::conditional<SMALL, f32x4, f32x16>::type acc_t;
+    acc_t c[kMixProducts];
 #pragma unroll
-    for (int i = 0; i < kMixProducts; ++i) c[i] = f32x16{};
+    for (int i = 0; i < kMixProducts; ++i) c[i] = acc_t{};
     float x[kMixProducts], s[kMixProducts];
 #pragma unroll
     for (int i = 0; i < kMixProducts; ++i) {
@@ -109,18 +114,25 @@ __global__ __launch_bounds__(kMixThreads, 1) void ceiling_mix_kernel(
         for (int i = 0; i < kMixProducts; ++i)
             a[i] = i < RD ? __builtin_bit_cast(bf16x8, set[512 * i]) : a_reg;
 #pragma unroll
-        for (int i = 0; i < kMixProducts; ++i)
-            c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, c[i], 0, 0, 0);
+        for (int i = 0; i < kMixProducts; ++i) {
+            if constexpr (SMALL)
+                c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, c[i], 0, 0, 0);
+            else
+                c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, c[i], 0, 0, 0);
+        }
         if constexpr (SM) {
-            float e[kMixProducts];
+            // the same VALU work per flop for both shapes: 8 elements per 8
+            // 32x32x16 products, 4 per 8 16x16x32 products
+            constexpr int NE = SMALL ? kMixProducts / 2 : kMixProducts;
+            float e[NE];
 #pragma unroll
-            for (int i = 0; i < kMixProducts; ++i) {
+            for (int i = 0; i < NE; ++i) {
                 x[i] = x[i] * 0.5f - 0.25f;
                 e[i] = __builtin_amdgcn_exp2f(x[i]);
                 s[i] += e[i];
             }
 #pragma unroll
-            for (int i = 0; i < kMixProducts; i += 2) {
+            for (int i = 0; i < NE; i += 2) {
                 const bf16x2 pair = {(__bf16)e[i], (__bf16)e[i + 1]};
                 pk ^= __builtin_bit_cast(uint32_t, pair);
             }
@@ -130,7 +142,7 @@ __global__ __launch_bounds__(kMixThreads, 1) void ceiling_mix_kernel(
 #pragma unroll
     for (int i = 0; i < kMixProducts; ++i)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) r += c[i][j];
+        for (int j = 0; j < (SMALL ? 4 : 16); ++j) r += c[i][j];
 #pragma unroll
     for (int i = 0; i < kMixProducts; ++i) r += s[i];
     r += (float)(pk & 1u);
@@ -140,12 +152,19 @@ __global__ __launch_bounds__(kMixThreads, 1) void ceiling_mix_kernel(
     out[(size_t)blockIdx.x * kMixThreads + threadIdx.x] = r;
 }
 
-template <int RD>
+template <int RD, bool SMALL>
 void launch_mix(bool sm, int n_wg, int iterations, const u32x4 *seed, float *out, hipStream_t st) {
     if (sm)
-        ceiling_mix_kernel<RD, true><<<n_wg, kMixThreads, 0, st>>>(seed, out, iterations);
+        ceiling_mix_kernel<RD, true, SMALL><<<n_wg, kMixThreads, 0, st>>>(seed, out, iterations);
     else
-        ceiling_mix_kernel<RD, false><<<n_wg, kMixThreads, 0, st>>>(seed, out, iterations);
+        ceiling_mix_kernel<RD, false, SMALL><<<n_wg, kMixThreads, 0, st>>>(seed, out, iterations);
+}
+
+template <int RD>
+void launch_mix(bool sm, bool small, int n_wg, int iterations, const u32x4 *seed, float *out,
+                hipStream_t st) {
+    if (small) launch_mix<RD, true>(sm, n_wg, iterations, seed, out, st);
+    else launch_mix<RD, false>(sm, n_wg, iterations, seed, out, st);
 }
 
 }  // namespace
@@ -172,24 +191,26 @@ extern "C" int fa_ceiling_read(const void *buf, size_t bytes, size_t chunk, uint
 }
 
 // reads_per_8: 0, 2, 4, 6 or 8 LDS operand reads per 8 products; softmax: 0
-// or 1; n_workgroups >= 1; iterations >= 1 (8 products per wave each);
-// seed: device, 8 KiB; out: device, n_workgroups * 512 floats.  Each launch
-// performs n_workgroups * 8 waves * iterations * 8 products of 32768 flop.
-extern "C" int fa_ceiling_mix(int reads_per_8, int softmax, int n_workgroups, int iterations,
-                              const void *seed, float *out, hipStream_t stream) {
+// or 1; shape: 0 for 32x32x16 products (32768 flop each), 1 for 16x16x32
+// (16384 flop each); n_workgroups >= 1; iterations >= 1 (8 products per wave
+// each); seed: device, 8 KiB; out: device, n_workgroups * 512 floats.  Each
+// launch performs n_workgroups * 8 waves * iterations * 8 products.
+extern "C" int fa_ceiling_mix(int reads_per_8, int softmax, int shape, int n_workgroups,
+                              int iterations, const void *seed, float *out, hipStream_t stream) {
     if (!seed || !out) return fail(1, "fa_ceiling_mix: null pointer");
     if (softmax != 0 && softmax != 1) return fail(1, "fa_ceiling_mix: softmax must be 0 or 1");
+    if (shape != 0 && shape != 1) return fail(1, "fa_ceiling_mix: shape must be 0 or 1");
     if (n_workgroups < 1) return fail(1, "fa_ceiling_mix: n_workgroups must be >= 1");
     if (iterations < 1) return fail(1, "fa_ceiling_mix: iterations must be >= 1");
     const u32x4 *sd = (const u32x4 *)seed;
-    const bool sm = softmax == 1;
+    const bool sm = softmax == 1, small = shape == 1;
     (void)hipGetLastError();
     switch (reads_per_8) {
-        case 0: launch_mix<0>(sm, n_workgroups, iterations, sd, out, stream); break;
-        case 2: launch_mix<2>(sm, n_workgroups, iterations, sd, out, stream); break;
-        case 4: launch_mix<4>(sm, n_workgroups, iterations, sd, out, stream); break;
-        case 6: launch_mix<6>(sm, n_workgroups, iterations, sd, out, stream); break;
-        case 8: launch_mix<8>(sm, n_workgroups, iterations, sd, out, stream); break;
+        case 0: launch_mix<0>(sm, small, n_workgroups, iterations, sd, out, stream); break;
+        case 2: launch_mix<2>(sm, small, n_workgroups, iterations, sd, out, stream); break;
+        case 4: launch_mix<4>(sm, small, n_workgroups, iterations, sd, out, stream); break;
+        case 6: launch_mix<6>(sm, small, n_workgroups, iterations, sd, out, stream); break;
+        case 8: launch_mix<8>(sm, small, n_workgroups, iterations, sd, out, stream); break;
         default: return fail(1, "fa_ceiling_mix: reads_per_8 must be 0, 2, 4, 6 or 8");
     }
     const hipError_t e = hipGetLastError();

@@ -89,6 +89,20 @@ __device__ __forceinline__ float sum_xor32(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes that hold one row in the
+// 16x16 product layouts) combined with max / sum; the lane ^ 16 step is a VALU
+// row swap: with both operands x, each lane receives x[l] and x[l ^ 16].
+__device__ __forceinline__ float row4_sum(float x)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return sum_xor32(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float row4_max(float x)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return max_xor32(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+
 // Sum over aligned groups of N lanes (N in 1,2,4,8,16,32); every lane of the
 // group receives the same value.  Order: pairs, quads, 8s, 16s, 32s.
 template <int N>

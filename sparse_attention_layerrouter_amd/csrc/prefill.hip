@@ -9,12 +9,18 @@
 //
 // bf16 kernel (head_dim 128 or 64): one workgroup of 8 wavefronts owns 256
 // query rows that share one KV head (GQA stacking: 4 heads x 64 positions when
-// G >= 4), so every K/V tile staged in LDS serves 256 rows.  Per 64-key tile:
-//   S^T = K Q^T  on v_mfma_f32_32x32x16_bf16 (K from LDS, Q^T in registers);
-//   online softmax in the exp2 domain, row statistics per lane;
-//   O^T += V^T P^T on the same MFMA; P^T comes straight out of the S^T
-//   accumulators (no cross-lane movement) and V^T is read from the row-major
-//   V tile by the transposing LDS read ds_read_b64_tr_b16.
+// G >= 4), so every K/V tile staged in LDS serves 256 rows.  Per 64-key tile
+// and wave (32 query rows, two row groups of 16):
+//   S^T = K Q^T  on v_mfma_f32_16x16x32_bf16 (K from LDS, Q^T in registers),
+//   each K fragment read once for both row groups;
+//   online softmax in the exp2 domain, row statistics per lane and row group;
+//   O^T += V^T P^T on the same MFMA, each V^T fragment read once for both row
+//   groups; P^T comes straight out of the S^T accumulators (no cross-lane
+//   movement) and V^T is read from the row-major V tile by the transposing
+//   LDS read ds_read_b64_tr_b16.
+// The 16x16x32 product moves a quarter of the accumulator bytes per flop of
+// the 32x32x16 one: under the board's power limit the kernel then runs at a
+// higher clock for the same LDS bytes and VALU work per flop.
 // The 8 waves form two groups that ping-pong: while one group's softmax keeps
 // the vector ALUs busy, the other group's QK and PV products keep the matrix
 // cores of the same SIMDs busy (one wave of each group per SIMD); a single
@@ -53,12 +59,14 @@ constexpr float kFastLimit = 65536.0f;  // largest p without a rescale
 // chunk c ^ f(r).
 //   K, read by ds_read_b128 with 16 rows per bank sweep at one logical chunk:
 //     fK(r) = r % (D/8)  -> the 16 rows hit 16 distinct chunks.
-//   V, read by ds_read_b64_tr_b16 with 4 rows x 32 bytes per 16-lane group:
-//     fV(r) = 4 (r % 4)  -> the 4 rows of a group land in disjoint chunk pairs.
+//   V, read by ds_read_b64_tr_b16 with 4 rows x 32 bytes per 16-lane group,
+//   the two groups of a 32-lane bank sweep 4 rows apart at the same columns:
+//     fV(r) = 4 (r % 4) ^ 2 ((r / 4) % 2)  -> the 8 rows of a sweep land in
+//     disjoint chunk pairs.
 template <int D>
 __device__ __forceinline__ int swz_k(int r) { return r & (D / 8 - 1); }
 template <int D>
-__device__ __forceinline__ int swz_v(int r) { return (4 * (r & 3)) & (D / 8 - 1); }
+__device__ __forceinline__ int swz_v(int r) { return (4 * (r & 3) ^ 2 * ((r >> 2) & 1)) & (D / 8 - 1); }
 
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int chunk, int swz)
@@ -122,9 +130,9 @@ struct TileLoader {
     }
 };
 
-__device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x16 &c)
+__device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c)
 {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 template <int V>
@@ -352,23 +360,31 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         *(u32x4 *)(v_lds1 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
     }
 
-    // ---- Q^T operand in registers: lane holds row pw0 + l32, d = ks*16 + half*8 ..
-    bf16x8 qreg[D / 16];
-    {
-        const int t = min(pw0 + l32, T - 1);
+    // ---- Q^T operand in registers: B operand of the 16x16x32 products, lane l
+    // holds row pw0 + 16 rg + l%16, d = 32 ks + 8 (l/16) .. +7
+    const int c16 = lane & 15, g4 = lane >> 4;
+    bf16x8 qreg[2][D / 32];
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+        const int t = min(pw0 + 16 * rg + c16, T - 1);
         const uint16_t *qr = q + ((size_t)(start_q + t - q_off) * hq + h) * D;
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            qreg[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qr + ks * 16 + half * 8));
+        for (int ks = 0; ks < D / 32; ++ks)
+            qreg[rg][ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qr + ks * 32 + g4 * 8));
     }
 
-    // masking thresholds for this wave
+    // masking thresholds for this wave and for the lane's two rows
     const int sink_tok = rule.ns << rule.bk_log2;
     const int win_lo_min = ((pw0 >> rule.bk_log2) - rule.nw + 1) << rule.bk_log2;
     const int win_lo_max = ((pw_last >> rule.bk_log2) - rule.nw + 1) << rule.bk_log2;
-    const int my_t = min(pw0 + l32, T - 1);  // query position of this lane's row
-    const int my_win_lo = ((my_t >> rule.bk_log2) - rule.nw + 1) << rule.bk_log2;
-    const bool my_dense = is_fa || my_t >= tail0;
+    int my_t[2], my_win_lo[2];
+    bool my_dense[2];
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+        my_t[rg] = min(pw0 + 16 * rg + c16, T - 1);
+        my_win_lo[rg] = ((my_t[rg] >> rule.bk_log2) - rule.nw + 1) << rule.bk_log2;
+        my_dense[rg] = is_fa || my_t[rg] >= tail0;
+    }
     // does any row of this wave see a key of the tile at k0 (list entry ent)?
     auto wave_sees = [&](int k0, uint32_t ent) __attribute__((always_inline)) {
         if constexpr (XA) {  // this wave's head kept the tile's block
@@ -379,91 +395,99 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         }
     };
 
-    // Per-lane LDS byte offsets, fixed for the whole kernel (the 32-key block
-    // and the k step only add constants, which become instruction offsets):
-    //   K operand of d step ks: key l32 (+32 for the second block), logical
-    //   chunk 2 ks + half, stored at chunk ^ swz_k(key) -- swz_k(key) depends on
-    //   l32 only.
-    //   V^T operand of d block dt: the transposed read of lane (a = (l%16)/4,
-    //   bq = l%4) points at key row 4 half + a (+16 per k step, +8 for the upper
-    //   4 keys), d columns C0 + 4 bq .. +3 with C0 = 32 dt + 16 ((l/16) % 2); the
-    //   instruction hands lane l the 4 keys of its group at d = C0 + l%16.  The
-    //   V swizzle depends on key row % 4 = a only.
-    uint32_t koff[D / 16];
+    // Per-lane LDS byte offsets, fixed for the whole kernel (the key group, the
+    // d step and the k step only add constants):
+    //   K operand (A of a 16x16x32 product) of key group kg, d step ks: key
+    //   16 kg + l%16, logical chunk 4 ks + l/16, stored at chunk ^ swz_k(key),
+    //   which depends on l%16 only.
+    //   V^T operand of d group dg, k step ksv: the transposed read of lane
+    //   (a = (l%16)/4, bq = l%4) points at key row 4 (l/16) + a (+32 per k step,
+    //   +16 for the upper 4 keys), d columns 16 dg + 4 bq .. +3; the instruction
+    //   hands lane l the 4 keys of its group at d = 16 dg + l%16.  The V swizzle
+    //   depends on key row % 8, i.e. on l.
+    uint32_t koff[D / 32];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-        koff[ks] = (uint32_t)tile_off<D>(l32, ks * 2 + half, swz_k<D>(l32));
-    uint32_t voff[D / 32];
+    for (int ks = 0; ks < D / 32; ++ks)
+        koff[ks] = (uint32_t)tile_off<D>(c16, ks * 4 + g4, swz_k<D>(c16));
+    uint32_t voff[D / 16];
     {
-        const int tr_a = (lane & 15) >> 2;
-        const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        const int r0 = 4 * half + tr_a;
+        const int r0 = 4 * g4 + (c16 >> 2);
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-            const int col = dt * 32 + tr_col;
-            voff[dt] = (uint32_t)(tile_off<D>(r0, col >> 3, swz_v<D>(r0)) + (col & 7) * 2);
+        for (int dg = 0; dg < D / 16; ++dg) {
+            const int col = dg * 16 + 4 * (c16 & 3);
+            voff[dg] = (uint32_t)(tile_off<D>(r0, col >> 3, swz_v<D>(r0)) + (col & 7) * 2);
         }
     }
 
-    f32x16 oacc[D / 32];
+    // O^T accumulators: oacc[dg][rg], lane l holds row 16 rg + l%16 at
+    // d = 16 dg + 4 (l/16) .. +3.  Row statistics per lane and row group.
+    f32x4 oacc[D / 16][2];
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-    float m_run = -INFINITY;  // reference max, log2 domain
-    float m_ref = 0.0f;       // the reference the scores are shifted by (0 while m_run = -inf)
-    float p_lim = -1.0f;      // fast-path bound on a lane's sum (-1: no reference yet)
-    float l_run = 0.0f;       // this lane's share of the row sum
-    f32x16 s[2];              // S^T of the current tile (two 32-key blocks)
-    uint32_t pk[2][8];        // P of the previous tile, bf16 pairs (0: none)
+    for (int i = 0; i < D / 16; ++i)
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int rg = 0; rg < 2; ++rg) oacc[i][rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[2] = {-INFINITY, -INFINITY};  // reference max, log2 domain
+    float m_ref[2] = {0.0f, 0.0f};            // the reference the scores are shifted by
+    float p_lim[2] = {-1.0f, -1.0f};          // fast-path bound on a lane's sum (-1: none yet)
+    float l_run[2] = {0.0f, 0.0f};            // this lane's share of the row sum
+    // S^T of the current tile: s[kg][rg], lane l holds row 16 rg + l%16 at keys
+    // 16 kg + 4 (l/16) .. +3
+    f32x4 s[4][2];
+    uint32_t pk[2][2][4];     // P of the previous tile, bf16 pairs, [k step][rg] (0: none)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pk[kb2][j] = 0u;
+    for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pk[a2][rg][j] = 0u;
     bool s_live = false;      // s holds a tile this wave sees
     int k0_live = 0;          // first key of the tile in s
 
     // ---- MFMA block of tile t: S^T = K Q^T of tile t, O^T += V^T P^T of tile t-1
-    // Operand reads from LDS: the K operand of d step ks / key block kb2, and
-    // the V^T operand of k step ksv / d block dt (two transposed reads).
-    // P^T for k-step ksv is the lane's own S^T values 8*(ksv%2) .. +8 of block
-    // ksv/2: k index 8*half + e <-> key 16*ksv + 8*(e/4) + 4*half + e%4.
-    auto k_operand = [&](const char *k_lds, int ks, int kb2) __attribute__((always_inline)) {
-        return __builtin_bit_cast(bf16x8, *(const u32x4 *)(k_lds + koff[ks] + kb2 * 32 * D * 2));
+    // P^T for k step ksv and row group rg is the lane's own S^T values of key
+    // groups 2 ksv and 2 ksv + 1: k index 8 (l/16) + e <-> key
+    // 32 ksv + 16 (e/4) + 4 (l/16) + e%4, the order the V^T reads follow.
+    auto k_operand = [&](const char *k_lds, int ks, int kg) __attribute__((always_inline)) {
+        return __builtin_bit_cast(bf16x8, *(const u32x4 *)(k_lds + koff[ks] + kg * 16 * D * 2));
     };
-    auto v_operand = [&](const char *v_lds, int ksv, int dt) __attribute__((always_inline)) {
-        const char *plo = v_lds + voff[dt] + ksv * 16 * D * 2;
+    auto v_operand = [&](const char *v_lds, int ksv, int dg) __attribute__((always_inline)) {
+        const char *plo = v_lds + voff[dg] + ksv * 32 * D * 2;
         i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4 *)plo);
         i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4 *)(plo + 8 * D * 2));
+            (__attribute__((address_space(3))) i16x4 *)(plo + 16 * D * 2));
         u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
         u32x4 aw = {lo2[0], lo2[1], hi2[0], hi2[1]};
         return __builtin_bit_cast(bf16x8, aw);
     };
-    auto p_operand = [&](int ksv) __attribute__((always_inline)) {
-        const int kb2 = ksv >> 1, jb = (ksv & 1) * 4;
-        u32x4 pw = {pk[kb2][jb], pk[kb2][jb + 1], pk[kb2][jb + 2], pk[kb2][jb + 3]};
+    auto p_operand = [&](int ksv, int rg) __attribute__((always_inline)) {
+        u32x4 pw = {pk[ksv][rg][0], pk[ksv][rg][1], pk[ksv][rg][2], pk[ksv][rg][3]};
         return __builtin_bit_cast(bf16x8, pw);
     };
-    // Both products run as one pipeline: round r issues the two QK MFMAs of d
-    // step r and two PV MFMAs, so six accumulator chains are in flight, and
-    // every operand is read kLook MFMAs ahead; scheduling barriers pin the
-    // order.  The block has no branches: a tile this wave does not see still
-    // runs QK (the result is dropped) and its P is zero, so PV adds exactly 0.
+    // Both products run as one pipeline of operand fragments: fragment f is a K
+    // fragment (f even) or a V^T fragment (f odd), each read from LDS kLook
+    // fragments ahead and used by the two products of its row groups;
+    // scheduling barriers pin the order.  The block has no branches: a tile this
+    // wave does not see still runs QK (the result is dropped) and its P is
+    // zero, so PV adds exactly 0.
     //
     // When LD is set (group 0 at even phases 2j) the block also issues the
-    // copies of K of tile j+1 and V of tile j, one every 4 MFMAs, so the memory
-    // pipeline drains while the matrix cores work and group 1's softmax is not
-    // interrupted.  Past the last tile the copies have an empty range (their
-    // buffers are not read again).
+    // copies of K of tile j+1 and V of tile j, one every two fragments, so the
+    // memory pipeline drains while the matrix cores work and group 1's softmax
+    // is not interrupted.  Past the last tile the copies have an empty range
+    // (their buffers are not read again).
     auto block_mfma = [&](auto ld_tag, const char *k_lds, const char *v_lds, int t, char *kdst,
                           char *vdst) __attribute__((always_inline)) {
         constexpr bool LD = decltype(ld_tag)::value != 0;
-        constexpr int NR = D / 16;       // rounds
-        constexpr int NM = 4 * NR;       // MFMAs
+        constexpr int NKS = D / 32;        // d steps of QK
+        constexpr int NKF = 4 * NKS;       // K fragments (4 key groups)
+        constexpr int NDG = D / 16;        // d groups of PV
+        constexpr int NVF = 2 * NDG;       // V^T fragments (2 k steps)
+        static_assert(NKF == NVF, "K and V fragments interleave one to one");
+        constexpr int NF = NKF + NVF;
         constexpr int kLook = 6;
-        constexpr int NDT = D / 32;
         constexpr int NLD = lk.NI + lv.NI;
-        static_assert(4 * NLD <= NM, "copies fit between the MFMAs");
+        static_assert(2 * NLD <= NF, "copies fit between the fragments");
         const int tc = min(t, n_tiles - 1);
         const uint32_t ent = XA ? xa_entry(tc) : 0u;
         const int k0_t = tile_k0e(tc, ent);
@@ -471,41 +495,43 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
         s_live = t < n_tiles && wave_sees(k0_t, ent);
         __amdgpu_buffer_rsrc_t rk, rv;
         if constexpr (LD) {
-            // past the last tile the copies get an empty range: they move no data
-            // (nobody reads those buffers again) and the workgroup's final wait
-            // for them is short
             rk = lk.rsrc(kb, row_stride, tile_k0(min(t + 1, n_tiles - 1)), t + 1 < n_tiles ? T : 0);
             rv = lv.rsrc(vb, row_stride, k0_t, t < n_tiles ? T : 0);
         }
-        s[0] = f32x16{};
-        s[1] = f32x16{};
-        bf16x8 ops[NM];
-        auto load_op = [&](int m) __attribute__((always_inline)) {
-            const int r = m >> 2, j = m & 3;
-            if (j < 2) {
-                ops[m] = k_operand(k_lds, r, j);
-            } else {
-                const int qv = 2 * r + (j - 2);
-                ops[m] = v_operand(v_lds, qv / NDT, qv % NDT);
-            }
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+            for (int rg = 0; rg < 2; ++rg) s[kg][rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 ops[NF];
+        // K fragment i: key group i / NKS, d step i % NKS (consecutive K
+        // fragments extend one S chain); V^T fragment i: d group i % NDG, k step
+        // i / NDG
+        auto load_op = [&](int f) __attribute__((always_inline)) {
+            const int i = f >> 1;
+            if ((f & 1) == 0) ops[f] = k_operand(k_lds, i % NKS, i / NKS);
+            else ops[f] = v_operand(v_lds, i / NDG, i % NDG);
         };
 #pragma unroll
-        for (int m = 0; m < kLook; ++m) load_op(m);
+        for (int f = 0; f < kLook; ++f) load_op(f);
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            const int r = m >> 2, j = m & 3;
-            if (j < 2) {
-                s[j] = mfma32(ops[m], qreg[r], s[j]);
+        for (int f = 0; f < NF; ++f) {
+            const int i = f >> 1;
+            if ((f & 1) == 0) {
+                const int ks = i % NKS, kg = i / NKS;
+#pragma unroll
+                for (int rg = 0; rg < 2; ++rg) s[kg][rg] = mfma16(ops[f], qreg[rg][ks], s[kg][rg]);
             } else {
-                const int qv = 2 * r + (j - 2);
-                oacc[qv % NDT] = mfma32(ops[m], p_operand(qv / NDT), oacc[qv % NDT]);
+                const int dg = i % NDG, ksv = i / NDG;
+#pragma unroll
+                for (int rg = 0; rg < 2; ++rg)
+                    oacc[dg][rg] = mfma16(ops[f], p_operand(ksv, rg), oacc[dg][rg]);
             }
-            if (m + kLook < NM) load_op(m + kLook);
+            if (f + kLook < NF) load_op(f + kLook);
             if constexpr (LD) {
-                if ((m & 3) == 1 && (m >> 2) < NLD) {
-                    const int i = m >> 2;
-                    if (i < lk.NI) lk.issue_one(i, kdst, rk);
-                    else lv.issue_one(i - lk.NI, vdst, rv);
+                if ((f & 1) == 1 && (f >> 1) < NLD) {
+                    const int c = f >> 1;
+                    if (c < lk.NI) lk.issue_one(c, kdst, rk);
+                    else lv.issue_one(c - lk.NI, vdst, rv);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -516,9 +542,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     auto block_valu = [&](int t) __attribute__((always_inline)) {
         if (!s_live) {
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
+            for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) pk[kb2][j] = 0u;
+                for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) pk[a2][rg][j] = 0u;
             return;
         }
         const int k0 = k0_live;  // tile t's first key, from its MFMA block
@@ -527,74 +555,88 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
                                (!w_dense_all && k0 < win_lo_max && k0 + kBN > sink_tok);
         if (need_mask) {
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
+            for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    int key = k0 + kb2 * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-                    bool vis = key <= my_t &&
-                               (my_dense || key < sink_tok || key >= my_win_lo);
-                    if (!vis) s[kb2][j] = -INFINITY;
-                }
+                for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int key = k0 + 16 * kg + 4 * g4 + j;
+                        const bool vis = key <= my_t[rg] &&
+                                         (my_dense[rg] || key < sink_tok || key >= my_win_lo[rg]);
+                        if (!vis) s[kg][rg][j] = -INFINITY;
+                    }
         }
-        // online softmax (exp2 domain) against a lazily moved reference m_ref.
-        // Fast path: p = 2^(s scale - m_ref) with the current reference; the
-        // lane's partial row sum bounds every p it holds, so if no lane's sum
-        // exceeds kFastLimit (and every row has a reference) nothing overflows
-        // and no rescale is needed.  Otherwise (rare: the first visible tile of
-        // a row, or scores that grew by many octaves) the tile max moves the
+        // online softmax (exp2 domain) against a lazily moved reference m_ref,
+        // per row group: the fast path p = 2^(s scale - m_ref) holds while no
+        // lane's partial row sum exceeds kFastLimit (which bounds every p it
+        // holds) and every row has a reference; otherwise the tile max moves the
         // reference, O and l are rescaled and p is recomputed.  O / l does not
-        // depend on the reference, so the result is the same softmax.
-        const float m_use = m_ref;
+        // depend on the reference.
+        const float m_use[2] = {m_ref[0], m_ref[1]};
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) s[kb2][j] = s[kb2][j] * scale_log2 - m_use;
+            for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s[kg][rg][j] = s[kg][rg][j] * scale_log2 - m_use[rg];
         __builtin_amdgcn_sched_barrier(0);
-        float e[32];
+        float e[2][16];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) e[i] = fast_exp2(s[i >> 4][i & 15]);
+        for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) e[rg][i] = fast_exp2(s[i >> 2][rg][i & 3]);
         __builtin_amdgcn_sched_barrier(0);
-        auto row_sum = [&]() __attribute__((always_inline)) {
-            float q1[16];
+        auto row_sum = [&](int rg) __attribute__((always_inline)) {
+            float q1[8];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) q1[i] = e[2 * i] + e[2 * i + 1];
+            for (int i = 0; i < 8; ++i) q1[i] = e[rg][2 * i] + e[rg][2 * i + 1];
 #pragma unroll
-            for (int w = 8; w >= 1; w >>= 1)
+            for (int w = 4; w >= 1; w >>= 1)
 #pragma unroll
                 for (int i = 0; i < w; ++i) q1[i] = q1[i] + q1[i + w];
             return q1[0];
         };
-        float psum = row_sum();
-        const bool fast = psum <= p_lim;  // NaN, or no reference yet: not fast
+        float psum[2] = {row_sum(0), row_sum(1)};
+        // NaN, or no reference yet: not fast
+        const bool fast = psum[0] <= p_lim[0] && psum[1] <= p_lim[1];
         if (__builtin_amdgcn_ballot_w64(!fast) != 0) {
-            float m1[11];
 #pragma unroll
-            for (int i = 0; i < 10; ++i) {
-                const int q = 3 * i;
-                m1[i] = fmaxf(fmaxf(s[q >> 4][q & 15], s[(q + 1) >> 4][(q + 1) & 15]),
-                              s[(q + 2) >> 4][(q + 2) & 15]);
+            for (int rg = 0; rg < 2; ++rg) {
+                float m1[4];
+#pragma unroll
+                for (int kg = 0; kg < 4; ++kg)
+                    m1[kg] = fmaxf(fmaxf(s[kg][rg][0], s[kg][rg][1]),
+                                   fmaxf(s[kg][rg][2], s[kg][rg][3]));
+                float mx = fmaxf(fmaxf(m1[0], m1[1]), fmaxf(m1[2], m1[3]));
+                mx = row4_max(mx) + m_use[rg];   // tile max in the log2 domain
+                const float m_new = fmaxf(m_run[rg], mx);
+                const float alpha =
+                    fast_exp2(m_run[rg] - (m_new == -INFINITY ? 0.0f : m_new));
+                l_run[rg] *= alpha;
+#pragma unroll
+                for (int i = 0; i < D / 16; ++i) oacc[i][rg] *= alpha;
+                m_run[rg] = m_new;
+                m_ref[rg] = m_new == -INFINITY ? 0.0f : m_new;
+                p_lim[rg] = m_new == -INFINITY ? -1.0f : kFastLimit;
+                const float shift = m_use[rg] - m_ref[rg];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) e[rg][i] = fast_exp2(s[i >> 2][rg][i & 3] + shift);
+                psum[rg] = row_sum(rg);
             }
-            m1[10] = fmaxf(s[1][14], s[1][15]);
-            float mx = fmaxf(fmaxf(fmaxf(m1[0], m1[1]), fmaxf(m1[2], m1[3])),
-                             fmaxf(fmaxf(m1[4], m1[5]), fmaxf(m1[6], m1[7])));
-            mx = fmaxf(mx, fmaxf(fmaxf(m1[8], m1[9]), m1[10]));
-            mx = max_xor32(mx) + m_use;   // tile max in the log2 domain
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.0f : m_new));
-            l_run *= alpha;
-#pragma unroll
-            for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
-            m_run = m_new;
-            m_ref = m_run == -INFINITY ? 0.0f : m_run;
-            p_lim = m_run == -INFINITY ? -1.0f : kFastLimit;
-            const float shift = m_use - m_ref;
-#pragma unroll
-            for (int i = 0; i < 32; ++i) e[i] = fast_exp2(s[i >> 4][i & 15] + shift);
-            psum = row_sum();
         }
+        // P^T of k step a2, row group rg: key groups 2 a2 and 2 a2 + 1
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pk[i >> 3][i & 7] = pack_bf16x2(e[2 * i], e[2 * i + 1]);
-        l_run += psum;
+        for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+            for (int rg = 0; rg < 2; ++rg) {
+                const float *e0 = &e[rg][8 * a2];
+                pk[a2][rg][0] = pack_bf16x2(e0[0], e0[1]);
+                pk[a2][rg][1] = pack_bf16x2(e0[2], e0[3]);
+                pk[a2][rg][2] = pack_bf16x2(e0[4], e0[5]);
+                pk[a2][rg][3] = pack_bf16x2(e0[6], e0[7]);
+            }
+        l_run[0] += psum[0];
+        l_run[1] += psum[1];
     };
 
     // ---- phases.  Even phase 2j: wait for this wave's copies, barrier, then
@@ -640,23 +682,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     if (!wave_active) return;
-    // ---- epilogue: O = O^T / l, lse = (m + log2 l) ln 2
-    const float l_tot = sum_xor32(l_run);
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const int t = pw0 + l32;
-    if (t < T) {
-        const size_t row = (size_t)(start_q + t - q_off);
-        uint16_t *orow = o + (row * hq + h) * D;
+    // ---- epilogue: O = O^T / l, lse = (m + log2 l) ln 2, per row group
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+    for (int rg = 0; rg < 2; ++rg) {
+        const float l_tot = row4_sum(l_run[rg]);
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        const int t = pw0 + 16 * rg + c16;
+        if (t < T) {
+            const size_t row = (size_t)(start_q + t - q_off);
+            uint16_t *orow = o + (row * hq + h) * D;
 #pragma unroll
-            for (int jg = 0; jg < 4; ++jg) {
-                int d = dt * 32 + 8 * jg + 4 * half;
-                u32x2 w = {pack_bf16x2(oacc[dt][4 * jg] * inv, oacc[dt][4 * jg + 1] * inv),
-                           pack_bf16x2(oacc[dt][4 * jg + 2] * inv, oacc[dt][4 * jg + 3] * inv)};
-                *(u32x2 *)(orow + d) = w;
+            for (int dg = 0; dg < D / 16; ++dg) {
+                const f32x4 &a4 = oacc[dg][rg];
+                u32x2 w = {pack_bf16x2(a4[0] * inv, a4[1] * inv),
+                           pack_bf16x2(a4[2] * inv, a4[3] * inv)};
+                *(u32x2 *)(orow + dg * 16 + 4 * g4) = w;
             }
-        if (lse && half == 0) lse[row * hq + h] = (m_run + fast_log2(l_tot)) * kLn2;
+            if (lse && g4 == 0) lse[row * hq + h] = (m_run[rg] + fast_log2(l_tot)) * kLn2;
+        }
     }
 }
 

@@ -46,19 +46,6 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// reductions over the 4 lanes l, l^16, l^32, l^48 that hold one reshaped row;
-// the lane ^ 16 step is a VALU row swap (no LDS round trip): with both operands
-// x, each lane receives x[l] and x[l ^ 16] in its two results
-__device__ __forceinline__ float row4_sum(float x)
-{
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return sum_xor32(__uint_as_float(r[0]) + __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float row4_max(float x)
-{
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return max_xor32(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
-}
 
 template <int V>
 using ic = std::integral_constant<int, V>;

@@ -33,21 +33,24 @@ def test_read_validation(buf, nbytes, chunk, sink, why):
     assert why in L.fa_ceiling_last_error().decode()
 
 
-@pytest.mark.parametrize("rd,sm,nwg,iters,seed,out,why", [
-    (3, 0, 1, 2, P, P, "reads_per_8"),
-    (10, 1, 1, 2, P, P, "reads_per_8"),
-    (8, 2, 1, 2, P, P, "softmax"),
-    (8, 1, 0, 2, P, P, "n_workgroups"),
-    (8, 1, 1, 0, P, P, "iterations"),
-    (8, 1, 1, 2, NULL, P, "null"),
-    (8, 1, 1, 2, P, NULL, "null"),
+@pytest.mark.parametrize("rd,sm,shape,nwg,iters,seed,out,why", [
+    (3, 0, 0, 1, 2, P, P, "reads_per_8"),
+    (10, 1, 0, 1, 2, P, P, "reads_per_8"),
+    (8, 2, 0, 1, 2, P, P, "softmax"),
+    (8, 1, 2, 1, 2, P, P, "shape"),
+    (8, 1, -1, 1, 2, P, P, "shape"),
+    (8, 1, 0, 0, 2, P, P, "n_workgroups"),
+    (8, 1, 1, 1, 0, P, P, "iterations"),
+    (8, 1, 0, 1, 2, NULL, P, "null"),
+    (8, 1, 1, 1, 2, P, NULL, "null"),
 ])
-def test_mix_validation(rd, sm, nwg, iters, seed, out, why):
+def test_mix_validation(rd, sm, shape, nwg, iters, seed, out, why):
     L = ceilings.lib()
-    assert L.fa_ceiling_mix(rd, sm, nwg, iters, seed, out, NULL) == 1
+    assert L.fa_ceiling_mix(rd, sm, shape, nwg, iters, seed, out, NULL) == 1
     assert why in L.fa_ceiling_last_error().decode()
 
 
 def test_mix_flop_count():
     # 2 workgroups x 8 waves x 3 iterations x 8 products x (32 x 32 x 16 x 2)
     assert ceilings.mix_flop(2, 3) == 2 * 8 * 3 * 8 * 32768
+    assert ceilings.mix_flop(2, 3, shape=1) == 2 * 8 * 3 * 8 * 16384

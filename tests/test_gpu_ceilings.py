@@ -1,7 +1,7 @@
 """The ceiling streams on the GPU: the read stream reads every 32-bit word of
 its buffer exactly once (the XOR of its per-thread results equals the XOR of
 the buffer, computed on the host), and the product stream runs every
-(read rate, softmax mix) variant with finite, repeatable output."""
+(shape, read rate, softmax mix) variant with finite, repeatable output."""
 import numpy as np
 import pytest
 
@@ -39,12 +39,13 @@ def test_product_stream_variants_run_and_repeat():
         np.uint16)
     seed = torch.from_numpy(bits.view(np.int16)).cuda()
     n_wg = 8
-    for rd in (0, 2, 4, 6, 8):
-        for sm in (False, True):
-            a = torch.empty(n_wg * 512, dtype=torch.float32, device="cuda")
-            b = torch.empty_like(a)
-            ceilings.fa_ceiling_mix(rd, sm, n_wg, 6, seed, a)
-            ceilings.fa_ceiling_mix(rd, sm, n_wg, 6, seed, b)
-            torch.cuda.synchronize()
-            assert torch.isfinite(a).all(), (rd, sm)
-            assert torch.equal(a, b), (rd, sm)
+    for shape in (0, 1):
+        for rd in (0, 2, 4, 6, 8):
+            for sm in (False, True):
+                a = torch.empty(n_wg * 512, dtype=torch.float32, device="cuda")
+                b = torch.empty_like(a)
+                ceilings.fa_ceiling_mix(rd, sm, n_wg, 6, seed, a, shape=shape)
+                ceilings.fa_ceiling_mix(rd, sm, n_wg, 6, seed, b, shape=shape)
+                torch.cuda.synchronize()
+                assert torch.isfinite(a).all(), (shape, rd, sm)
+                assert torch.equal(a, b), (shape, rd, sm)
