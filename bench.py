@@ -284,7 +284,8 @@ def main():
         return
     stream = torch.cuda.current_stream()
     ceil = None
-    if args.only_ceilings or not (args.no_ceilings or args.profile):
+    if args.only_ceilings or not (args.no_ceilings or args.profile or args.only_qwen
+                                  or args.cpu_full):
         ceil = ceilings_leg(stream)
         if args.only_ceilings:
             print(json.dumps({"ceilings": ceil}))
@@ -876,8 +877,8 @@ def main():
         },
     }
     if ceil is not None:
-        ceil["fa_prefill_over_softmax_mix_stream"] = round(
-            achieved_tflops / ceil["mix"]["softmax_mix_1_read_tflops"], 4)
+        ceil["fa_prefill_over_its_mix_stream"] = round(
+            achieved_tflops / ceil["mix"]["prefill_mix_tflops"], 4)
         ceil["fa_decode_over_read_stream"] = round(achieved_gbs / ceil["read"]["best_gbs"], 4)
         if xattn is not None:
             ceil["xa_scores_iid_over_small_product_stream"] = round(
@@ -958,9 +959,11 @@ def ceilings_leg(stream):
     read of 1 KiB per product, without and with the online softmax's VALU mix
     (one exponential, one FMA, one add and half a bf16 pair pack per product;
     the FA prefill kernel issues one exponential and about 2.6 other VALU
-    instructions and 1 KiB of LDS reads per product), and 16x16x32 products
-    with 0 or 1 read per product (the XAttention score kernel's mix: one 1 KiB
-    read per 16x16x32 product and little VALU work)."""
+    instructions and 1 KiB of LDS reads per 32x32x16-sized product), and
+    16x16x32 products with 0, 1/2 or 1 read per product, without and with the
+    same softmax work per flop (the FA prefill kernel's own mix is 16x16x32
+    with one 1 KiB read per two products; the XAttention score kernel's is one
+    read per 16x16x32 product with little VALU work)."""
     from sparse_attention_layerrouter_amd import ceilings
 
     ceilings.lib()
@@ -973,6 +976,9 @@ def ceilings_leg(stream):
         return [r for r in mx["streams"] if r["shape"] == shape and r["softmax_mix"] == sm
                 and r["lds_reads_per_product"] == reads][0]["tflops"]
 
+    # the FA prefill kernel's mix: 16x16x32 products, one 1 KiB LDS fragment per two
+    # products, the softmax's VALU work per flop
+    mx["prefill_mix_tflops"] = pick("16x16x32", 0.5, True)
     mx["softmax_mix_1_read_tflops"] = pick("32x32x16", 1.0, True)
     mx["products_only_tflops"] = pick("32x32x16", 0.0, False)
     mx["small_1_read_tflops"] = pick("16x16x32", 1.0, False)

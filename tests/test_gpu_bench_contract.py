@@ -37,6 +37,6 @@ def test_bench_prints_one_contract_line():
     assert 0 < roof["frac"] < 1 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert d["decode"]["tok_s"] > 0
     c = d["ceilings"]
-    assert c["read"]["best_gbs"] > 0 and c["mix"]["softmax_mix_1_read_tflops"] > 0
-    assert 0 < c["fa_prefill_over_softmax_mix_stream"] and 0 < c["fa_decode_over_read_stream"]
+    assert c["read"]["best_gbs"] > 0 and c["mix"]["prefill_mix_tflops"] > 0
+    assert 0 < c["fa_prefill_over_its_mix_stream"] and 0 < c["fa_decode_over_read_stream"]
     assert d["timing"]["prefill_fa_layer_ms"]["n"] >= 1
