@@ -381,10 +381,21 @@ def main():
             rec.append(((e_r0, e_r1), pre, dec))
 
     if args.profile:
-        # kernel-only run for counter passes: layer 0 FA, layer 1 SA (prefill and decode)
+        # kernel-only run for counter passes: layer 0 FA, layer 1 SA (prefill and decode),
+        # then the XAttention score kernel
         for _ in range(2):
             step(prefill_route=torch.tensor([[1, 0] + [0] * 30], dtype=torch.uint8, device=dev))
         torch.cuda.synchronize()
+        # the XAttention score kernel at the same length (block 128, stride 8), twice
+        XBp, XSp = 128, 8
+        nqb_p = (T + XBp - 1) // XBp
+        sc_p = torch.empty((1, HQ, nqb_p, nqb_p), dtype=torch.float32, device=dev)
+        xw_p = torch.empty(_lib.fa_xattn_workspace_size(1, HQ, nqb_p), dtype=torch.uint8,
+                           device=dev)
+        for _ in range(2):
+            _lib.fa_xattn_scores(sets[0][0], sets[0][1], cu, T, XBp, XSp, scale, sc_p, xw_p)
+        torch.cuda.synchronize()
+        del sc_p, xw_p
         kept_sa = kept_tokens_decode(NC, False)
         alg = {
             "prefill_bf16_fa_131k": {"flop": flops_of_pairs(pairs_fa(T))},
@@ -393,6 +404,8 @@ def main():
                                     "bytes": NB * HKV * NC * D * 4 + 2 * NB * HQ * D * 2},
             "decode_bf16_sa_131k": {"flop": 4.0 * NB * HQ * kept_sa * D,
                                     "bytes": NB * HKV * kept_sa * D * 4 + 2 * NB * HQ * D * 2},
+            "xa_score_131k": {"flop": float(HQ * (nqb_p * (nqb_p + 1) // 2) * 16 * 16 * (XSp * D)
+                                            * 2)},
         }
         print(json.dumps({"profile_run": True, "seq": T, "decode_cache": NC,
                           "decode_batch": NB, "algorithmic": alg}))
@@ -982,7 +995,8 @@ def ceilings_leg(stream):
     mx["softmax_mix_1_read_tflops"] = pick("32x32x16", 1.0, True)
     mx["products_only_tflops"] = pick("32x32x16", 0.0, False)
     mx["small_1_read_tflops"] = pick("16x16x32", 1.0, False)
-    return {"read": rd, "mix": mx}
+    log("ceiling streams: VALU issue")
+    return {"read": rd, "mix": mx, "valu": ceilings.measure_valu(stream)}
 
 
 def config2_leg(stream, qkv):

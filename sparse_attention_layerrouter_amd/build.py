@@ -57,9 +57,10 @@ def _resources(stderr: str) -> dict:
     return out
 
 
-def _compile(src: str):
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, csrc: str = CSRC, build_dir: str = BUILD_DIR):
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    flags = [f if f != CSRC else csrc for f in FLAGS]
+    cmd = [HIPCC, *flags, "-c", os.path.join(csrc, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
     else:
@@ -87,6 +88,16 @@ def _link(objs: list, out: str) -> None:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
+
+
+def build_copy(csrc: str, out: str, build_dir: str) -> str:
+    """Build the attention library from another source directory (a patched copy of
+    csrc/, e.g. an instrumented one for measurement) into `out`; the same flags."""
+    os.makedirs(build_dir, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        done = list(ex.map(lambda src: _compile(src, csrc, build_dir), SOURCES))
+    _link([o for o, _ in done], out)
+    return out
 
 
 def build(verbose: bool = False) -> str:

@@ -15,7 +15,7 @@ import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfa_ceilings.so")
-EXPORTS = ("fa_ceiling_last_error", "fa_ceiling_read", "fa_ceiling_mix")
+EXPORTS = ("fa_ceiling_last_error", "fa_ceiling_read", "fa_ceiling_mix", "fa_ceiling_valu")
 
 MIX_THREADS = 512
 MIX_WAVES = 8
@@ -42,6 +42,8 @@ def lib() -> ctypes.CDLL:
     L.fa_ceiling_read.argtypes = [P, SZ, SZ, P, P]
     L.fa_ceiling_mix.restype = I32
     L.fa_ceiling_mix.argtypes = [I32, I32, I32, I32, I32, P, P, P]
+    L.fa_ceiling_valu.restype = I32
+    L.fa_ceiling_valu.argtypes = [I32, I32, I32, I32, P, P, P]
     _lib = L
     return L
 
@@ -76,6 +78,16 @@ def fa_ceiling_mix(reads_per_8: int, softmax: bool, n_workgroups: int, iteration
     _check(lib().fa_ceiling_mix(reads_per_8, 1 if softmax else 0, shape, n_workgroups, iterations,
                                 ctypes.c_void_p(seed.data_ptr()), ctypes.c_void_p(out.data_ptr()),
                                 _stream_ptr(stream)))
+
+
+def fa_ceiling_valu(kind: int, n_workgroups: int, threads: int, iterations: int, out, cycles,
+                    stream=None) -> None:
+    """One launch of the VALU issue stream (kind 0 FMA, 1 exponential, 2 both);
+    out: n_workgroups * threads floats, cycles: n_workgroups * threads / 32 int64
+    (per wave: loop shader-clock ticks, loop realtime ticks)."""
+    _check(lib().fa_ceiling_valu(kind, n_workgroups, threads, iterations,
+                                 ctypes.c_void_p(out.data_ptr()),
+                                 ctypes.c_void_p(cycles.data_ptr()), _stream_ptr(stream)))
 
 
 def mix_flop(n_workgroups: int, iterations: int, shape: int = 0) -> float:
@@ -148,3 +160,51 @@ def measure_mix(stream, configs=((0, False, 0), (8, False, 0), (6, False, 0), (4
                     "tflops": round(flop / med / 1e9, 1)})
     torch.cuda.synchronize()
     return {"workgroups": n_workgroups, "iterations": iterations, "streams": res}
+
+
+VALU_KINDS = {0: "fma", 1: "exp", 2: "exp_and_fma"}
+# waves per SIMD -> (workgroups, threads) on a 256-CU board with 4 SIMDs per CU
+VALU_LAYOUTS = {1: (256, 256), 2: (512, 256), 8: (512, 1024)}
+
+
+def measure_valu(stream, iterations: int = 4000) -> dict:
+    """VALU issue rates for three launch layouts (nominally 1, 2 and 8 waves per
+    SIMD on a 256-CU board).  Per kind: wave_cycles_per_instruction, the median
+    wave's loop shader-clock ticks / its instructions (the interval between one
+    wave's instructions under whatever shares its SIMD); simd_cycles_per_instruction,
+    the launch's wall time x the loop clock x 1024 SIMDs / all waves' instructions
+    (the SIMD's throughput, with no assumption about which waves were resident
+    together); and the clock (ticks / realtime)."""
+    import torch
+
+    dev = torch.device("cuda", torch.cuda.current_device())
+    res = {}
+    for wps, (nwg, threads) in VALU_LAYOUTS.items():
+        with torch.cuda.stream(stream):
+            out = torch.empty(nwg * threads, dtype=torch.float32, device=dev)
+            cyc = torch.empty(nwg * threads // 32, dtype=torch.int64, device=dev)
+        row = {}
+        for kind, name in VALU_KINDS.items():
+            fa_ceiling_valu(kind, nwg, threads, iterations, out, cyc, stream)  # warm-up
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fa_ceiling_valu(kind, nwg, threads, iterations, out, cyc, stream)
+            b.record(stream)
+            b.synchronize()
+            wall_s = a.elapsed_time(b) * 1e-3
+            c = cyc.cpu().view(-1, 2)
+            order = sorted(range(c.shape[0]), key=lambda i: int(c[i, 0]))
+            mid = order[len(order) // 2]
+            ticks, real = int(c[mid, 0]), int(c[mid, 1])
+            clock = ticks / (real * 10.0) if real else None  # GHz (realtime: 100 MHz)
+            instr = iterations * 64 * (2 if kind == 2 else 1)
+            waves = nwg * threads // 64
+            row[name] = {
+                "wave_cycles_per_instruction": round(ticks / instr, 3),
+                "simd_cycles_per_instruction": (round(wall_s * clock * 1e9 * 1024 / (waves * instr), 3)
+                                                if clock else None),
+                "clock_ghz": round(clock, 3) if clock else None}
+        res[f"{wps}_waves_per_simd_nominal"] = row
+    return {"iterations": iterations, "chains_per_lane": 8, "steps_per_iteration": 8,
+            "layouts": res}

@@ -19,6 +19,12 @@
 //    else the CU issues; this stream has no dependences between the three
 //    kinds of work, no barriers and no global traffic, so it is the rate that
 //    a kernel with the same mix can reach at best.
+//  * fa_ceiling_valu times VALU issue alone: each lane runs 8 independent
+//    chains of FMAs, of exponentials (v_exp_f32), or of both interleaved, and
+//    each wave writes its loop's shader-clock ticks (s_memtime) and realtime
+//    ticks (s_memrealtime, 100 MHz): with the workgroup size and count chosen
+//    for 1, 2 or 8 waves per SIMD, the ticks per wave instruction on a SIMD and
+//    the clock the loop ran at.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -33,6 +39,8 @@ int fa_ceiling_read(const void *buf, size_t bytes, size_t chunk, uint32_t *sink,
                     hipStream_t stream);
 int fa_ceiling_mix(int reads_per_8, int softmax, int shape, int n_workgroups, int iterations,
                    const void *seed, float *out, hipStream_t stream);
+int fa_ceiling_valu(int kind, int n_workgroups, int threads, int iterations, float *out,
+                    unsigned long long *cycles, hipStream_t stream);
 }
 
 namespace {
@@ -167,9 +175,72 @@ void launch_mix(bool sm, bool small, int n_wg, int iterations, const u32x4 *seed
     else launch_mix<RD, false>(sm, n_wg, iterations, seed, out, st);
 }
 
+constexpr int kValuChains = 8;
+constexpr int kValuUnroll = 8;
+
+// KIND 0: x = x * a + b (FMA); 1: x = 2^(-x) (v_exp_f32 with a negated input,
+// which converges to about 0.64); 2: both, one after the other, per chain.
+// Every chain is independent, so the issue rate alone sets the pace.  Each
+// wave writes (shader-clock ticks, realtime ticks) of its loop.
+template <int KIND>
+__global__ __launch_bounds__(1024) void ceiling_valu_kernel(
+    float *__restrict__ out, unsigned long long *__restrict__ cycles, int iterations) {
+    float x[kValuChains];
+#pragma unroll
+    for (int i = 0; i < kValuChains; ++i) x[i] = 0.25f + 0.001f * (float)(threadIdx.x + i);
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+    const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iterations; ++it) {
+        // 8 steps of every chain per iteration, so the loop branch is amortised
+#pragma unroll
+        for (int u = 0; u < kValuUnroll; ++u)
+#pragma unroll
+            for (int i = 0; i < kValuChains; ++i) {
+                if constexpr (KIND == 0 || KIND == 2) x[i] = __builtin_fmaf(x[i], 0.999f, 0.0001f);
+                if constexpr (KIND == 1 || KIND == 2) x[i] = __builtin_amdgcn_exp2f(-x[i]);
+            }
+    }
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+    const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+    float r = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kValuChains; ++i) r += x[i];
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = r;
+    if ((threadIdx.x & 63) == 0) {
+        const size_t w = (size_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+        cycles[2 * w] = t1 - t0;
+        cycles[2 * w + 1] = r1 - r0;
+    }
+}
+
 }  // namespace
 
 extern "C" const char *fa_ceiling_last_error(void) { return g_err; }
+
+// kind: 0 FMA chains, 1 exponential chains, 2 both interleaved; n_workgroups
+// of `threads` threads (a multiple of 64, at most 1024); iterations >= 1 (64
+// chain steps per lane each: 8 chains x 8); out: device, n_workgroups * threads floats;
+// cycles: device, 2 values per wave (n_workgroups * threads / 32): its loop's
+// shader-clock ticks, then its realtime (100 MHz) ticks.
+extern "C" int fa_ceiling_valu(int kind, int n_workgroups, int threads, int iterations,
+                               float *out, unsigned long long *cycles, hipStream_t stream) {
+    if (!out || !cycles) return fail(1, "fa_ceiling_valu: null pointer");
+    if (kind < 0 || kind > 2) return fail(1, "fa_ceiling_valu: kind must be 0, 1 or 2");
+    if (n_workgroups < 1) return fail(1, "fa_ceiling_valu: n_workgroups must be >= 1");
+    if (threads < 64 || threads > 1024 || threads % 64 != 0)
+        return fail(1, "fa_ceiling_valu: threads must be a multiple of 64 up to 1024");
+    if (iterations < 1) return fail(1, "fa_ceiling_valu: iterations must be >= 1");
+    (void)hipGetLastError();
+    if (kind == 0)
+        ceiling_valu_kernel<0><<<n_workgroups, threads, 0, stream>>>(out, cycles, iterations);
+    else if (kind == 1)
+        ceiling_valu_kernel<1><<<n_workgroups, threads, 0, stream>>>(out, cycles, iterations);
+    else
+        ceiling_valu_kernel<2><<<n_workgroups, threads, 0, stream>>>(out, cycles, iterations);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(4, hipGetErrorString(e));
+    return 0;
+}
 
 // buf: device, bytes long, 16-byte aligned; chunk: bytes per workgroup, a
 // multiple of 32 KiB dividing bytes; sink: device, (bytes / chunk) * 256

@@ -42,6 +42,7 @@ HOT_KERNELS = {
                             ("decode.hip", "fa_common.h", "fa_launch.h")),
     "decode_bf16_sa_131k": ("decode_bf16_kernel<128, 4, 2, false, true>",
                             ("decode.hip", "fa_common.h", "fa_launch.h")),
+    "xa_score_131k": ("xa_score_kernel<128, 8>", ("xattn.hip", "fa_common.h")),
 }
 COPY_BYTES = 1 << 30
 

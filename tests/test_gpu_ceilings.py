@@ -1,7 +1,9 @@
 """The ceiling streams on the GPU: the read stream reads every 32-bit word of
 its buffer exactly once (the XOR of its per-thread results equals the XOR of
 the buffer, computed on the host), and the product stream runs every
-(shape, read rate, softmax mix) variant with finite, repeatable output."""
+(shape, read rate, softmax mix) variant with finite, repeatable output, and the
+VALU issue stream runs each kind with finite, repeatable output and every wave's
+cycle count written."""
 import numpy as np
 import pytest
 
@@ -49,3 +51,21 @@ def test_product_stream_variants_run_and_repeat():
                 torch.cuda.synchronize()
                 assert torch.isfinite(a).all(), (shape, rd, sm)
                 assert torch.equal(a, b), (shape, rd, sm)
+
+
+def test_valu_stream_kinds_run_and_repeat():
+    import torch
+
+    from sparse_attention_layerrouter_amd import ceilings
+
+    for n_wg, threads in ((4, 1024), (3, 256)):
+        for kind in (0, 1, 2):
+            a = torch.empty(n_wg * threads, dtype=torch.float32, device="cuda")
+            b = torch.empty_like(a)
+            cyc = torch.zeros(n_wg * threads // 32, dtype=torch.int64, device="cuda")
+            ceilings.fa_ceiling_valu(kind, n_wg, threads, 50, a, cyc)
+            ceilings.fa_ceiling_valu(kind, n_wg, threads, 50, b, cyc)
+            torch.cuda.synchronize()
+            assert torch.isfinite(a).all(), kind
+            assert torch.equal(a, b), kind
+            assert (cyc.view(-1, 2)[:, 0] > 0).all(), kind  # every wave wrote its ticks
